@@ -1,0 +1,437 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU oracle of the MoE layer
+ * forward.  TEST INFRASTRUCTURE ONLY: it exists so tests, the smoke check and
+ * the benchmark's CPU baseline can check the HIP path.  The product path never
+ * links, loads or calls it, and it shares no code, header or table with it.
+ *
+ * Sources (the pages this follows):
+ *  [TRT]  "TensorRT-LLM 源码完全拆解(十三): MoE 层前向执行——路由、Fused Kernel 与
+ *         专家并行的三段拼装", sections "MoE 在推理侧到底特殊在哪里" (the layer
+ *         formula y = sum_{i in TopK(x)} g_i(x) E_i(x) and the shared expert),
+ *         "路由方法枚举" (RoutingMethodType comments), "DeepSeek-V3 的 noaux_tc"
+ *         (sigmoid, bias for selection only, top-2 group sums, group mask,
+ *         unbiased renormalisation + 1e-20 + routed scaling factor),
+ *         "权重加载" (fused gate/up projection, gated activation expands FC1
+ *         to 2*I), "小结" (FC1 -> act -> FC2 then apply weights / finalize).
+ *  [VLLM] "vLLM 源码完全拆解(八): MoE 层的前向执行", sections "FusedTopKRouter"
+ *         (softmax -> top-k -> optional renormalise) and "专家权重如何存储"
+ *         (w13 [E, 2I, H], w2 [E, H, I]).
+ *  [GG]   "从 Dense GEMM 到 TP MoE 的演进逻辑" (gsyq.cn), sections 2.1-2.2
+ *         (offset array marking each group's start; permute of each
+ *         expert's tokens into one contiguous block).
+ *
+ * Readings of points the pages leave open (each also listed in the design
+ * notes of the repository):
+ *  - Softmax methods select on the fp32 logits (softmax is strictly monotone,
+ *    so the top-k set is the same in exact arithmetic).
+ *  - Ties: lower expert index wins; lower group index wins for groups; the k
+ *    ids of a token are listed in selection order (key desc, index asc).
+ *  - DeepSeek-V3 sigmoid is the fp64 value 1/(1+exp(-l)) rounded once to
+ *    fp32; values within 2^-45 (relative) of an fp32 rounding midpoint are
+ *    re-evaluated in long double and counted ("hard cases").
+ *  - The biased key and the group score are single fp32 additions.
+ *  - Default honours an explicit renormalise flag (vLLM FusedTopKRouter).
+ *  - The 1e-20 guard applies to DeepSeek-V3 only; the routed scaling factor
+ *    multiplies every method's scales (1.0 unless given).
+ *  - w13 rows [0, I) are the gate projection, rows [I, 2I) the up projection;
+ *    SwiGLU h = silu(gate) * up with silu(z) = z / (1 + exp(-z)).
+ *  - fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of
+ *    each [out, in] matrix.
+ *  - The shared expert is group E (+s), weight 1.0, rows P + s*T + t.
+ *
+ * All floating point is fp64 except where the method itself fixes fp32 (the
+ * selection keys).  Inputs in bf16/fp8/fp32 are decoded exactly to fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "moe_oracle.h"
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double oracle_decode_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP float8 e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; exponent 0 is subnormal (m/8 * 2^-6). */
+double oracle_decode_e4m3(uint8_t bits)
+{
+    int sign = (bits >> 7) & 1;
+    int e = (bits >> 3) & 0xF;
+    int m = bits & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+static double load_elem(const void* base, int dtype, size_t i)
+{
+    switch (dtype) {
+    case ORACLE_F32:
+        return (double)((const float*)base)[i];
+    case ORACLE_BF16:
+        return oracle_decode_bf16(((const uint16_t*)base)[i]);
+    default:
+        return oracle_decode_e4m3(((const uint8_t*)base)[i]);
+    }
+}
+
+/* ---------------------------------------------------------------- routing */
+
+typedef struct {
+    float key;
+    int idx;
+} cand_t;
+
+/* Order: larger key first; equal keys -> smaller index first. */
+static int cand_cmp(const void* pa, const void* pb)
+{
+    const cand_t* a = (const cand_t*)pa;
+    const cand_t* b = (const cand_t*)pb;
+    if (a->key > b->key) return -1;
+    if (a->key < b->key) return 1;
+    return (a->idx < b->idx) ? -1 : (a->idx > b->idx);
+}
+
+/* fp32 sigmoid defined as the fp64 sigmoid rounded once to fp32; near a
+ * rounding midpoint the fp64 value is not trusted and long double decides. */
+float oracle_sigmoid_f32(float l, int* hard)
+{
+    double v = 1.0 / (1.0 + exp(-(double)l));
+    float f = (float)v;
+    double up = 0.5 * ((double)f + (double)nextafterf(f, INFINITY));
+    double dn = 0.5 * ((double)f + (double)nextafterf(f, -INFINITY));
+    double tol = ldexp(fabs(v), -45);
+    if (fabs(v - up) <= tol || fabs(v - dn) <= tol) {
+        long double lv = 1.0L / (1.0L + expl(-(long double)l));
+        f = (float)lv;
+        if (hard) *hard += 1;
+    }
+    return f;
+}
+
+/* Routing of one token.  ids/scales receive k entries in selection order. */
+static void route_token(const float* l, int E, int method, int k, int n_group,
+                        int topk_group, const float* bias, double scaling,
+                        int renorm, int32_t* ids, double* scales, int* hard,
+                        cand_t* c /* scratch [E] */, float* sig /* scratch [E] */)
+{
+    if (method == ORACLE_DEEPSEEKV3) {
+        /* scores = sigmoid(logits); biased keys decide selection only. */
+        int gsz = E / n_group;
+        cand_t gc[256];
+        unsigned char gsel[256];
+        float keyv[256];
+        for (int e = 0; e < E; ++e) {
+            sig[e] = oracle_sigmoid_f32(l[e], hard);
+            keyv[e] = sig[e] + (bias ? bias[e] : 0.0f); /* one fp32 add */
+        }
+        /* group score = sum of the two largest biased keys of the group */
+        for (int g = 0; g < n_group; ++g) {
+            for (int i = 0; i < gsz; ++i) {
+                c[i].key = keyv[g * gsz + i];
+                c[i].idx = g * gsz + i;
+            }
+            qsort(c, (size_t)gsz, sizeof(cand_t), cand_cmp);
+            gc[g].key = c[0].key + c[1].key; /* one fp32 add */
+            gc[g].idx = g;
+        }
+        /* keep the topk_group best groups */
+        qsort(gc, (size_t)n_group, sizeof(cand_t), cand_cmp);
+        memset(gsel, 0, sizeof gsel);
+        for (int i = 0; i < topk_group; ++i)
+            gsel[gc[i].idx] = 1;
+        /* top-k experts among the kept groups (others masked out) */
+        int n = 0;
+        for (int e = 0; e < E; ++e) {
+            if (gsel[e / gsz]) {
+                c[n].key = keyv[e];
+                c[n].idx = e;
+                ++n;
+            }
+        }
+        qsort(c, (size_t)n, sizeof(cand_t), cand_cmp);
+        /* weights from the unbiased scores of the chosen experts */
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j)
+            sum += (double)sig[c[j].idx];
+        sum += 1e-20;
+        for (int j = 0; j < k; ++j) {
+            ids[j] = c[j].idx;
+            scales[j] = (double)sig[c[j].idx] / sum * scaling;
+        }
+        return;
+    }
+
+    /* softmax family: the top-k set is selected on the fp32 logits */
+    for (int e = 0; e < E; ++e) {
+        c[e].key = l[e];
+        c[e].idx = e;
+    }
+    qsort(c, (size_t)E, sizeof(cand_t), cand_cmp);
+    for (int j = 0; j < k; ++j)
+        ids[j] = c[j].idx;
+
+    if (method == ORACLE_RENORMALIZE) {
+        /* TopK -> Softmax over the selected logits only */
+        double m = (double)c[0].key, z = 0.0;
+        for (int j = 0; j < k; ++j)
+            z += exp((double)c[j].key - m);
+        for (int j = 0; j < k; ++j)
+            scales[j] = exp((double)c[j].key - m) / z;
+    } else {
+        /* Default: Softmax over all experts -> TopK (-> renormalise when the
+         * flag asks).  RenormalizeNaive: Softmax -> TopK -> Renormalize. */
+        double m = (double)c[0].key, z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp((double)l[e] - m);
+        double zs = 0.0;
+        for (int j = 0; j < k; ++j) {
+            scales[j] = exp((double)c[j].key - m) / z;
+            zs += scales[j];
+        }
+        if (method == ORACLE_RENORMALIZE_NAIVE || renorm)
+            for (int j = 0; j < k; ++j)
+                scales[j] /= zs;
+    }
+    for (int j = 0; j < k; ++j)
+        scales[j] *= scaling;
+}
+
+int oracle_route(const float* logits, int T, int E, int method, int k, int n_group,
+                 int topk_group, const float* bias, double scaling, int renorm,
+                 int32_t* ids, double* scales, int64_t* hard_cases)
+{
+    if (E < 1 || E > 256 || k < 1 || k > E)
+        return -1;
+    if (method == ORACLE_DEEPSEEKV3) {
+        if (n_group < 1 || E % n_group || topk_group < 1 || topk_group > n_group ||
+            E / n_group < 2 || k > topk_group * (E / n_group))
+            return -1;
+    } else if (method != ORACLE_DEFAULT && method != ORACLE_RENORMALIZE &&
+               method != ORACLE_RENORMALIZE_NAIVE) {
+        return -1;
+    }
+    cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)E);
+    float* sig = (float*)malloc(sizeof(float) * (size_t)E);
+    int hard = 0;
+    for (int t = 0; t < T; ++t)
+        route_token(logits + (size_t)t * E, E, method, k, n_group, topk_group, bias,
+                    scaling, renorm, ids + (size_t)t * k, scales + (size_t)t * k, &hard, c,
+                    sig);
+    free(c);
+    free(sig);
+    if (hard_cases) *hard_cases = hard;
+    return 0;
+}
+
+/* ---------------------------------------------------------------- permute */
+
+/* Counting sort of the flat pairs p = t*k + j by expert id, stable in p.
+ * offsets[g] = first row of group g; routed groups hold P rows in total,
+ * shared group E+s holds rows P + s*T + t in token order. */
+int oracle_permute(const int32_t* ids, int T, int k, int E, int n_shared,
+                   int32_t* offsets, int32_t* permuted_pair, int32_t* unpermute)
+{
+    int P = T * k;
+    int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    for (int g = 0; g <= E + n_shared; ++g)
+        offsets[g] = 0;
+    for (int p = 0; p < P; ++p) {
+        if (ids[p] < 0 || ids[p] >= E) {
+            free(seen);
+            return -1;
+        }
+        offsets[ids[p] + 1] += 1;
+    }
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] += offsets[e];
+    for (int s = 0; s < n_shared; ++s)
+        offsets[E + s + 1] = offsets[E + s] + T;
+    for (int p = 0; p < P; ++p) {
+        int e = ids[p];
+        int row = offsets[e] + seen[e]++;
+        permuted_pair[row] = p;
+        unpermute[p] = row;
+    }
+    free(seen);
+    return 0;
+}
+
+/* ------------------------------------------------------------- expert FFN */
+
+/* Weight of group g, matrix [rows, cols], element (r, c), dequantised. */
+static double weight_at(const void* w, int wdt, const float* scale, int g, int rows, int cols,
+                        int r, int c)
+{
+    size_t i = ((size_t)g * rows + r) * cols + c;
+    double v = load_elem(w, wdt, i);
+    if (wdt == ORACLE_FP8) {
+        int sr = rows / 128, sc = cols / 128;
+        v *= (double)scale[((size_t)g * sr + r / 128) * sc + c / 128];
+    }
+    return v;
+}
+
+/* Expert g applied to one activation row a[H]:
+ *   gate = W1 a, up = W3 a (rows [0,I) and [I,2I) of w13[g]),
+ *   h = silu(gate) * up, out = W2 h.  h_out (may be NULL) receives h. */
+static void expert_apply(const oracle_weights* W, int g, const double* a, double* h,
+                         double* out)
+{
+    int H = W->H, I = W->I;
+    for (int i = 0; i < I; ++i) {
+        double gate = 0.0, up = 0.0;
+        for (int c = 0; c < H; ++c) {
+            gate += weight_at(W->w13, W->wdt, W->w13_scale, g, 2 * I, H, i, c) * a[c];
+            up += weight_at(W->w13, W->wdt, W->w13_scale, g, 2 * I, H, I + i, c) * a[c];
+        }
+        h[i] = gate / (1.0 + exp(-gate)) * up;
+    }
+    for (int o = 0; o < H; ++o) {
+        double acc = 0.0;
+        for (int i = 0; i < I; ++i)
+            acc += weight_at(W->w2, W->wdt, W->w2_scale, g, H, I, o, i) * h[i];
+        out[o] = acc;
+    }
+}
+
+static void load_row(const void* x, int act, int H, int t, double* a)
+{
+    for (int c = 0; c < H; ++c)
+        a[c] = load_elem(x, act, (size_t)t * H + c);
+}
+
+/* Output rows of the expert FFN for the permuted rows listed in `rows`:
+ * row r belongs to the group g with offsets[g] <= r < offsets[g+1]; its token
+ * is permuted_pair[r] / k for routed groups and r - offsets[g] for shared
+ * ones.  out: [n_rows, H];  h_out (nullable): [n_rows, I]. */
+int oracle_expert_rows(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+                       int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
+                       const int32_t* rows, int n_rows, double* h_out, double* out)
+{
+    int G = E + n_shared;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int i = 0; i < n_rows; ++i) {
+        int r = rows[i];
+        int g = -1;
+        for (int q = 0; q < G; ++q)
+            if (offsets[q] <= r && r < offsets[q + 1]) g = q;
+        if (g < 0) {
+            bad += 1;
+            continue;
+        }
+        int t = (g < E) ? permuted_pair[r] / k : r - offsets[g];
+        double* a = (double*)malloc(sizeof(double) * (size_t)W->H);
+        double* h = (double*)malloc(sizeof(double) * (size_t)W->I);
+        load_row(x, act, W->H, t, a);
+        expert_apply(W, g, a, h, out + (size_t)i * W->H);
+        if (h_out)
+            memcpy(h_out + (size_t)i * W->I, h, sizeof(double) * (size_t)W->I);
+        free(a);
+        free(h);
+    }
+    (void)T;
+    return bad ? -1 : 0;
+}
+
+/* The layer by its definition, for the tokens listed in `tokens`:
+ *   y_t = sum_j scales[t,j] * E_{ids[t,j]}(x_t)  +  sum_s E_{E+s}(x_t).
+ * No permute is involved.  y: [n_tokens, H]. */
+int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+                        int n_shared, const int32_t* ids, const double* scales,
+                        const int32_t* tokens, int n_tokens, double* y)
+{
+    int H = W->H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int i = 0; i < n_tokens; ++i) {
+        int t = tokens[i];
+        if (t < 0 || t >= T) {
+            bad += 1;
+            continue;
+        }
+        double* a = (double*)malloc(sizeof(double) * (size_t)H);
+        double* h = (double*)malloc(sizeof(double) * (size_t)W->I);
+        double* o = (double*)malloc(sizeof(double) * (size_t)H);
+        double* yt = y + (size_t)i * H;
+        load_row(x, act, H, t, a);
+        for (int c = 0; c < H; ++c)
+            yt[c] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            expert_apply(W, ids[(size_t)t * k + j], a, h, o);
+            for (int c = 0; c < H; ++c)
+                yt[c] += scales[(size_t)t * k + j] * o[c];
+        }
+        for (int s = 0; s < n_shared; ++s) {
+            expert_apply(W, E + s, a, h, o);
+            for (int c = 0; c < H; ++c)
+                yt[c] += o[c];
+        }
+        free(a);
+        free(h);
+        free(o);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------- finalize */
+
+/* y_t = sum_j scales[t,j] * fc2[unpermute[t*k+j]] + sum_s fc2[P + s*T + t].
+ * fc2: [R, H] in `dt`; y: [T, H] fp64. */
+int oracle_finalize(const void* fc2, int dt, const int32_t* unpermute, const double* scales,
+                    int T, int k, int H, int n_shared, double* y)
+{
+    size_t P = (size_t)T * k;
+    for (int t = 0; t < T; ++t) {
+        double* yt = y + (size_t)t * H;
+        for (int c = 0; c < H; ++c)
+            yt[c] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            size_t row = (size_t)unpermute[(size_t)t * k + j];
+            for (int c = 0; c < H; ++c)
+                yt[c] += scales[(size_t)t * k + j] * load_elem(fc2, dt, row * H + c);
+        }
+        for (int s = 0; s < n_shared; ++s) {
+            size_t row = P + (size_t)s * T + t;
+            for (int c = 0; c < H; ++c)
+                yt[c] += load_elem(fc2, dt, row * H + c);
+        }
+    }
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
