@@ -1,0 +1,209 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward.
+ *
+ * The layer computes, for every token t with activation x_t,
+ *     y_t = sum_{i in TopK(x_t)} g_i(x_t) * E_i(x_t)   (+ shared experts)
+ * ("TensorRT-LLM 源码完全拆解(十三): MoE 层前向执行", section "MoE 在推理侧到底特殊在
+ * 哪里"), as four asynchronous calls on one HIP stream:
+ *
+ *   moe_route      router logits -> (expert ids int32 [T,k], scales fp32 [T,k])
+ *   moe_permute    counting sort of the T*k (token, expert) pairs into
+ *                  contiguous per-expert row blocks + offsets
+ *   moe_expert_ffn grouped GEMM FC1 with fused SwiGLU, then grouped GEMM FC2
+ *   moe_finalize   weighted gather-sum of each token's k FFN rows (+ shared)
+ *
+ * Conventions shared by every call:
+ *  - Pointers named as device buffers are device pointers (hipMalloc'd or
+ *    torch CUDA tensors); scalars are passed by value.  All arrays are dense,
+ *    row-major, contiguous.
+ *  - The caller owns and allocates every buffer, including the workspace
+ *    (sized by moe_workspace_size); the library never allocates device
+ *    memory on these paths.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    kernels and return; nothing synchronises the device and no value is read
+ *    back to the host, so the sequence can be captured into a HIP graph.
+ *  - Argument errors are detected on the host before anything is launched and
+ *    returned as a status; moe_last_error() then gives the reason.  A failed
+ *    kernel launch returns MOE_ERR_DEVICE.  There is no fallback path: shapes
+ *    outside the kernels' limits return MOE_ERR_UNSUPPORTED (the pages'
+ *    position: a fused kernel has hard shape limits and the caller must be
+ *    told, section "融合算子与回退阈值").
+ *  - T == 0 is valid: the call returns MOE_OK and launches nothing.
+ *  - Not thread-safe per stream: calls that overlap on one stream or share a
+ *    workspace race.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* inconsistent sizes, null required pointer, bad enum */
+    MOE_ERR_UNSUPPORTED = 2, /* valid request outside the kernels' limits */
+    MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_workspace_size */
+    MOE_ERR_DEVICE = 4       /* a HIP call or kernel launch failed */
+} moe_status;
+
+/* Routing methods, numbered as the RoutingMethodType enum on the TensorRT-LLM
+ * page (section "路由方法枚举"). */
+typedef enum moe_route_method {
+    MOE_ROUTE_DEFAULT = 0,           /* softmax over all E -> top-k          */
+    MOE_ROUTE_RENORMALIZE = 1,       /* top-k -> softmax over the k kept     */
+    MOE_ROUTE_DEEPSEEKV3 = 2,        /* noaux_tc grouped sigmoid routing     */
+    MOE_ROUTE_RENORMALIZE_NAIVE = 4  /* softmax -> top-k -> renormalise      */
+} moe_route_method;
+
+/* Honoured by MOE_ROUTE_DEFAULT only: divide the k kept probabilities by their
+ * sum (the renormalize switch of vLLM's FusedTopKRouter). */
+#define MOE_ROUTE_FLAG_RENORMALIZE 1u
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Shape limits of the kernels (the expert-count and top-k limits of the fused
+ * routing kernel on the TensorRT-LLM page, section "融合算子与回退阈值"; its
+ * 32-expert group-size limit does not apply here: groups go through LDS). */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+
+/*
+ * moe_route -- per-token expert selection and weights.
+ * TensorRT-LLM page, sections "路由方法枚举" and "DeepSeek-V3 的 noaux_tc";
+ * vLLM page ("vLLM 源码完全拆解(八)"), section "FusedTopKRouter".
+ *
+ *  logits   device fp32 [T, E]   router scores.
+ *  method   moe_route_method.
+ *  k        experts per token, 1 <= k <= min(E, 8).
+ *  n_group, topk_group   DeepSeek-V3 only: E is split into n_group equal
+ *           groups of E/n_group >= 2 experts; a group scores the sum of its
+ *           two largest biased keys; the topk_group best groups are kept and
+ *           the k experts are chosen among them (k <= topk_group * E/n_group).
+ *           Ignored by the other methods.
+ *  bias     device fp32 [E] or NULL (= zeros); DeepSeek-V3 only: added to the
+ *           sigmoid scores for selection, never to the weights.
+ *  scaling  multiplies every returned scale (routed scaling factor; pass 1.0
+ *           when the model has none).
+ *  flags    MOE_ROUTE_FLAG_RENORMALIZE (DEFAULT only).
+ *  ids      device int32 [T, k] out: chosen experts, ordered by key
+ *           descending, ties to the lower expert index (groups likewise).
+ *  scales   device fp32 [T, k] out: weights of `ids`, same order.
+ * Selection precision: softmax methods select on the fp32 logits (softmax is
+ * monotone); DeepSeek-V3 selects on fl32(sigmoid) + bias with the sigmoid
+ * evaluated in fp64 and rounded once to fp32.  Weights are computed in fp64
+ * and rounded once.  NaN logits give unspecified (but in-bounds) ids.
+ */
+moe_status moe_route(const float* logits, int T, int E, int method, int k, int n_group,
+                     int topk_group, const float* bias, float scaling, unsigned flags,
+                     int32_t* ids, float* scales, void* stream);
+
+/*
+ * moe_permute -- counting sort of the P = T*k pairs p = t*k + j by expert id,
+ * stable in p, giving each expert one contiguous block of rows ("从 Dense GEMM
+ * 到 TP MoE 的演进逻辑", section 2.1: one offset array marks where each group
+ * starts; section 2.2: permute each expert's tokens into one block).
+ *
+ *  ids            device int32 [T, k]; values must lie in [0, E) (values
+ *                 outside are clamped into range: memory-safe, not meaningful).
+ *  n_shared       shared experts (every token, weight 1) appended as groups
+ *                 E .. E+n_shared-1; shared group s owns rows P + s*T + t.
+ *  expert_offsets device int32 [E + n_shared + 1] out: first row of each group;
+ *                 expert_offsets[E] == P, last entry == P + n_shared*T.
+ *  permuted_pair  device int32 [P] out: row -> pair index p.
+ *  unpermute      device int32 [P] out: pair index p -> row.
+ *  ws, ws_bytes   device workspace of at least
+ *                 moe_workspace_size(T, k, E, n_shared, H, I, act) bytes (any
+ *                 H, I, act: the permute scratch does not depend on them).
+ * Integer results are bit-exact and deterministic.
+ */
+moe_status moe_permute(const int32_t* ids, int T, int k, int E, int n_shared,
+                       int32_t* expert_offsets, int32_t* permuted_pair, int32_t* unpermute,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- every group's expert FFN on its rows, as two grouped GEMMs
+ * over one flattened list of (group, M-tile, N-tile) work items ("从 Dense GEMM
+ * 到 TP MoE 的演进逻辑", section 2.2: tile scheduling over all groups):
+ *     h_r   = silu(W1_g x_t) * (W3_g x_t)        (FC1 + SwiGLU, kept in ws)
+ *     out_r = W2_g h_r                           (FC2)
+ * for every row r of group g (token t = permuted_pair[r] / k, or r - offset
+ * for shared groups).  Weight layout of the vLLM page, section "专家权重如何存
+ * 储"; gated expansion of FC1 to 2*I of the TensorRT-LLM page, section "权重加
+ * 载".
+ *
+ *  x          device [T, H] in `act` (MOE_F32 or MOE_BF16).
+ *  H, I       hidden and intermediate sizes, multiples of 128.
+ *  expert_offsets, permuted_pair   as produced by moe_permute.
+ *  w13        device [E + n_shared, 2I, H] in `wdt`: rows [0, I) are the gate
+ *             projection W1, rows [I, 2I) the up projection W3.
+ *  w2         device [E + n_shared, H, I] in `wdt`.
+ *  wdt        MOE_F32 (with act MOE_F32), MOE_BF16 or MOE_FP8_E4M3 (OCP e4m3fn,
+ *             with act MOE_BF16).
+ *  w13_scale  device fp32 [E + n_shared, 2I/128, H/128] for fp8 (else NULL):
+ *             the weight is code * scale of its 128x128 block.
+ *  w2_scale   device fp32 [E + n_shared, H/128, I/128] for fp8 (else NULL).
+ *  fc2_out    device [T*k + n_shared*T, H] out, in `act`: FFN output per row
+ *             (unweighted).
+ *  ws         device workspace (moe_workspace_size bytes) holding h.
+ * Accumulation is fp32; h and fc2_out are rounded once to `act`.
+ */
+moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, int E,
+                          int n_shared, const int32_t* expert_offsets,
+                          const int32_t* permuted_pair, const void* w13, const void* w2,
+                          int wdt, const float* w13_scale, const float* w2_scale,
+                          void* fc2_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_finalize -- y_t = sum_j scales[t,j] * fc2_out[unpermute[t*k+j]]
+ *                       + sum_s fc2_out[T*k + s*T + t]
+ * accumulated in fp32 in j order, rounded once to `ydt`; a gather, no atomics,
+ * so results are deterministic.  The routing weight is applied here, after
+ * FC2 (TensorRT-LLM page, sections "通信与计算融合的方向" and "小结").
+ *
+ *  fc2_out    device [T*k + n_shared*T, H] in `dt` (MOE_F32 or MOE_BF16).
+ *  unpermute, scales   from moe_permute / moe_route.
+ *  y          device [T, H] out in `ydt` (MOE_F32 or MOE_BF16).
+ *  H          multiple of 8.
+ */
+moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
+                        const float* scales, int T, int k, int H, int n_shared, void* y,
+                        int ydt, void* stream);
+
+/* Bytes of workspace that moe_permute and moe_expert_ffn need for this shape
+ * (0 on invalid arguments).  One buffer of this size serves both calls. */
+size_t moe_workspace_size(int T, int k, int E, int n_shared, int H, int I, int act);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* Reason for the last non-OK status returned on the calling thread. */
+const char* moe_last_error(void);
+
+/*
+ * Per-kernel timing (measurement support, off by default).  When enabled,
+ * every launch is bracketed by two HIP events recorded on the launch stream;
+ * moe_kernel_times() waits for the recorded events and returns, per kernel
+ * id, the summed milliseconds and the launch count since the last reset.
+ */
+enum {
+    MOE_KID_ROUTE = 0,
+    MOE_KID_PERMUTE_COUNT = 1,
+    MOE_KID_PERMUTE_SCAN = 2,
+    MOE_KID_PERMUTE_SCATTER = 3,
+    MOE_KID_FC1 = 4,
+    MOE_KID_FC2 = 5,
+    MOE_KID_FINALIZE = 6,
+    MOE_NUM_KIDS = 7
+};
+moe_status moe_timing_enable(int enable);
+moe_status moe_kernel_times(double* ms /*[MOE_NUM_KIDS]*/, int64_t* launches /*[MOE_NUM_KIDS]*/,
+                            int reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

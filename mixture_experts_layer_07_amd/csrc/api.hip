@@ -1,0 +1,288 @@
+// C ABI of libmoe: argument validation, workspace sizing, error reporting and
+// per-kernel timing.  Every check runs on the host before anything is
+// launched; the launchers in the kernel sources assume validated arguments.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+moe_status set_error(moe_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status launch_status(const char* what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return set_error(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+int device_cu_count()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// ------------------------------------------------------------------ timing
+namespace {
+struct TimingState {
+    std::mutex mu;
+    bool enabled = false;
+    struct Rec { int kid; hipEvent_t a, b; };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> free_events;
+    double ms[MOE_NUM_KIDS] = {0};
+    int64_t n[MOE_NUM_KIDS] = {0};
+};
+TimingState& timing()
+{
+    static TimingState t;
+    return t;
+}
+hipEvent_t take_event(TimingState& t)
+{
+    if (!t.free_events.empty()) {
+        hipEvent_t e = t.free_events.back();
+        t.free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+TimedLaunch::TimedLaunch(int kid, hipStream_t s) : kid_(kid), s_(s), slot_(-1)
+{
+    TimingState& t = timing();
+    if (!t.enabled) return;
+    std::lock_guard<std::mutex> g(t.mu);
+    hipEvent_t a = take_event(t), b = take_event(t);
+    if (!a || !b) return;
+    t.pending.push_back({kid, a, b});
+    slot_ = (int)t.pending.size() - 1;
+    (void)hipEventRecord(a, s);
+}
+
+TimedLaunch::~TimedLaunch()
+{
+    if (slot_ < 0) return;
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    (void)hipEventRecord(t.pending[slot_].b, s_);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+bool valid_act(int d) { return d == MOE_F32 || d == MOE_BF16; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+moe_status check_common(int T, int k, int E, int n_shared)
+{
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (E < 1) return set_error(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+    if (E > MOE_MAX_EXPERTS)
+        return set_error(MOE_ERR_UNSUPPORTED, "E = %d exceeds the kernel limit %d", E, MOE_MAX_EXPERTS);
+    if (k < 1 || k > E) return set_error(MOE_ERR_INVALID_ARG, "k must be in [1, E] (k=%d, E=%d)", k, E);
+    if (k > MOE_MAX_TOPK)
+        return set_error(MOE_ERR_UNSUPPORTED, "k = %d exceeds the kernel limit %d", k, MOE_MAX_TOPK);
+    if (n_shared < 0 || n_shared > 64)
+        return set_error(MOE_ERR_INVALID_ARG, "n_shared must be in [0, 64] (got %d)", n_shared);
+    const long long R = (long long)T * k + (long long)n_shared * T;
+    if (R > (1ll << 30))
+        return set_error(MOE_ERR_UNSUPPORTED, "T*k + n_shared*T = %lld rows exceeds 2^30", R);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int st)
+{
+    switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or type outside the kernels' limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: HIP call or kernel launch failed";
+    default: return "unknown moe_status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_size(int T, int k, int E, int n_shared, int H, int I, int act)
+{
+    (void)H;
+    if (check_common(T, k, E, n_shared) != MOE_OK || I < 0 || !valid_act(act)) return 0;
+    const size_t a = align256(permute_scratch_bytes(T, k, E));
+    const size_t b = ffn_scratch_bytes(T, k, n_shared, I, act);
+    return (a > b ? a : b) + 256;
+}
+
+moe_status moe_route(const float* logits, int T, int E, int method, int k, int n_group,
+                     int topk_group, const float* bias, float scaling, unsigned flags,
+                     int32_t* ids, float* scales, void* stream)
+{
+    moe_status st = check_common(T, k, E, 0);
+    if (st != MOE_OK) return st;
+    if (method == 3 || (method >= 5 && method <= 8))
+        return set_error(MOE_ERR_UNSUPPORTED, "routing method %d is not implemented (supported: 0, 1, 2, 4)", method);
+    if (method != MOE_ROUTE_DEFAULT && method != MOE_ROUTE_RENORMALIZE &&
+        method != MOE_ROUTE_DEEPSEEKV3 && method != MOE_ROUTE_RENORMALIZE_NAIVE)
+        return set_error(MOE_ERR_INVALID_ARG, "unknown routing method %d", method);
+    if (flags & ~MOE_ROUTE_FLAG_RENORMALIZE)
+        return set_error(MOE_ERR_INVALID_ARG, "unknown routing flags 0x%x", flags);
+    if (!isfinite(scaling)) return set_error(MOE_ERR_INVALID_ARG, "scaling must be finite");
+    if (method == MOE_ROUTE_DEEPSEEKV3) {
+        if (n_group < 1 || E % n_group != 0)
+            return set_error(MOE_ERR_INVALID_ARG, "n_group=%d must divide E=%d", n_group, E);
+        const int gsz = E / n_group;
+        if (gsz < 2)
+            return set_error(MOE_ERR_INVALID_ARG, "groups need >= 2 experts for the top-2 group score (E/n_group=%d)", gsz);
+        if (topk_group < 1 || topk_group > n_group)
+            return set_error(MOE_ERR_INVALID_ARG, "topk_group=%d must be in [1, n_group=%d]", topk_group, n_group);
+        if (k > topk_group * gsz)
+            return set_error(MOE_ERR_INVALID_ARG, "k=%d exceeds the experts of the kept groups (%d)", k, topk_group * gsz);
+    }
+    if (T == 0) return MOE_OK;
+    if (!logits || !ids || !scales)
+        return set_error(MOE_ERR_INVALID_ARG, "logits, ids and scales must be non-null");
+    return launch_route(logits, T, E, method, k, n_group, topk_group,
+                        method == MOE_ROUTE_DEEPSEEKV3 ? bias : nullptr, scaling, flags, ids,
+                        scales, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const int32_t* ids, int T, int k, int E, int n_shared,
+                       int32_t* expert_offsets, int32_t* permuted_pair, int32_t* unpermute,
+                       void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_common(T, k, E, n_shared);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!ids || !expert_offsets || !permuted_pair || !unpermute)
+        return set_error(MOE_ERR_INVALID_ARG,
+                         "ids, expert_offsets, permuted_pair and unpermute must be non-null");
+    const size_t need = permute_scratch_bytes(T, k, E);
+    if (!ws || ws_bytes < need)
+        return set_error(MOE_ERR_WORKSPACE, "permute needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    return launch_permute(ids, T, k, E, n_shared, expert_offsets, permuted_pair, unpermute, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, int E,
+                          int n_shared, const int32_t* expert_offsets,
+                          const int32_t* permuted_pair, const void* w13, const void* w2,
+                          int wdt, const float* w13_scale, const float* w2_scale,
+                          void* fc2_out, void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_common(T, k, E, n_shared);
+    if (st != MOE_OK) return st;
+    if (!valid_act(act)) return set_error(MOE_ERR_INVALID_ARG, "activation dtype %d must be MOE_F32 or MOE_BF16", act);
+    if (wdt != MOE_F32 && wdt != MOE_BF16 && wdt != MOE_FP8_E4M3)
+        return set_error(MOE_ERR_INVALID_ARG, "unknown weight dtype %d", wdt);
+    if (H < 1 || I < 1) return set_error(MOE_ERR_INVALID_ARG, "H and I must be positive (H=%d, I=%d)", H, I);
+    if (H % 128 || I % 128)
+        return set_error(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (H=%d, I=%d)", H, I);
+    if (act == MOE_F32 && wdt != MOE_F32)
+        return set_error(MOE_ERR_UNSUPPORTED, "fp32 activations need fp32 weights");
+    if (act == MOE_BF16 && wdt == MOE_F32)
+        return set_error(MOE_ERR_UNSUPPORTED, "bf16 activations need bf16 or fp8 weights");
+    if (wdt == MOE_FP8_E4M3 && (!w13_scale || !w2_scale))
+        return set_error(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !w13 || !w2 || !fc2_out || (E > 0 && !permuted_pair))
+        return set_error(MOE_ERR_INVALID_ARG, "x, expert_offsets, permuted_pair, w13, w2 and fc2_out must be non-null");
+    const size_t need = ffn_scratch_bytes(T, k, n_shared, I, act);
+    if (!ws || ws_bytes < need)
+        return set_error(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    return launch_ffn(x, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2, wdt,
+                      wdt == MOE_FP8_E4M3 ? w13_scale : nullptr,
+                      wdt == MOE_FP8_E4M3 ? w2_scale : nullptr, fc2_out, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
+                        const float* scales, int T, int k, int H, int n_shared, void* y,
+                        int ydt, void* stream)
+{
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (k < 1) return set_error(MOE_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+    if (k > MOE_MAX_TOPK) return set_error(MOE_ERR_UNSUPPORTED, "k = %d exceeds the kernel limit %d", k, MOE_MAX_TOPK);
+    if (n_shared < 0 || n_shared > 64) return set_error(MOE_ERR_INVALID_ARG, "n_shared must be in [0, 64]");
+    if (!valid_act(dt) || !valid_act(ydt))
+        return set_error(MOE_ERR_INVALID_ARG, "fc2_out and y dtypes must be MOE_F32 or MOE_BF16");
+    if (H < 1) return set_error(MOE_ERR_INVALID_ARG, "H must be positive");
+    if (H % 8) return set_error(MOE_ERR_UNSUPPORTED, "H must be a multiple of 8 (got %d)", H);
+    if ((long long)T * k + (long long)n_shared * T > (1ll << 30))
+        return set_error(MOE_ERR_UNSUPPORTED, "too many rows");
+    if (T == 0) return MOE_OK;
+    if (!fc2_out || !unpermute || !scales || !y)
+        return set_error(MOE_ERR_INVALID_ARG, "fc2_out, unpermute, scales and y must be non-null");
+    return launch_finalize(fc2_out, dt, unpermute, scales, T, k, H, n_shared, y, ydt,
+                           static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_timing_enable(int enable)
+{
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.enabled = enable != 0;
+    return MOE_OK;
+}
+
+moe_status moe_kernel_times(double* ms, int64_t* launches, int reset)
+{
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (auto& r : t.pending) {
+        if (hipEventSynchronize(r.b) != hipSuccess)
+            return set_error(MOE_ERR_DEVICE, "hipEventSynchronize failed while reading kernel times");
+        float v = 0.f;
+        if (hipEventElapsedTime(&v, r.a, r.b) == hipSuccess) {
+            t.ms[r.kid] += v;
+            t.n[r.kid] += 1;
+        }
+        t.free_events.push_back(r.a);
+        t.free_events.push_back(r.b);
+    }
+    t.pending.clear();
+    for (int i = 0; i < MOE_NUM_KIDS; ++i) {
+        if (ms) ms[i] = t.ms[i];
+        if (launches) launches[i] = t.n[i];
+        if (reset) {
+            t.ms[i] = 0;
+            t.n[i] = 0;
+        }
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

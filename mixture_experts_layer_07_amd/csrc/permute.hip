@@ -1,0 +1,153 @@
+// moe_permute: stable counting sort of the T*k (token, expert) pairs by expert.
+//
+// Gathering each expert's rows into one contiguous block, with an offset array
+// marking where each group starts, is the layout the grouped GEMM needs
+// ("从 Dense GEMM 到 TP MoE 的演进逻辑", sections 2.1 and 2.2).
+//
+// Three small kernels over fixed chunks of kChunk consecutive pairs:
+//   count    per-chunk histogram of expert ids (LDS counters)
+//   scan     per expert, exclusive scan of its chunk counts -> the base row of
+//            each (chunk, expert); exclusive scan over experts -> offsets
+//   scatter  one wavefront per chunk walks its pairs in order, 64 at a time;
+//            lanes holding the same expert find each other with one ballot per
+//            id bit, take rank = #peers on lower lanes, and the highest peer
+//            advances that expert's running base.  Pair order is kept, so the
+//            result equals a stable sort: bit-exact and deterministic.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;
+
+__device__ __forceinline__ int clamp_id(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+__global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ ids,
+                                                            int P, int E,
+                                                            int32_t* __restrict__ counts)
+{
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int p0 = blockIdx.x * kChunk;
+    const int p1 = min(P, p0 + kChunk);
+    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&hist[clamp_id(ids[p], E)], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One block of 256 threads: thread e owns expert e (E <= 256).
+__global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ counts,
+                                                           int nchunks, int T, int P, int E,
+                                                           int n_shared,
+                                                           int32_t* __restrict__ offsets)
+{
+    __shared__ int tot[256];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = counts[(size_t)c * E + e];
+            counts[(size_t)c * E + e] = run;
+            run += v;
+        }
+    }
+    tot[e] = (e < E) ? run : 0;
+    __syncthreads();
+    // inclusive scan over experts (Hillis-Steele)
+    for (int d = 1; d < 256; d <<= 1) {
+        const int v = (e >= d) ? tot[e - d] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    const int base = (e < E) ? tot[e] - run : 0;
+    if (e < E) {
+        offsets[e] = base;
+        for (int c = 0; c < nchunks; ++c) counts[(size_t)c * E + e] += base;
+    }
+    if (e == 0) {
+        offsets[E] = P;
+        for (int s = 0; s < n_shared; ++s) offsets[E + s + 1] = P + (s + 1) * T;
+    }
+}
+
+// One wavefront per chunk.
+__global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __restrict__ ids,
+                                                             int P, int E,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ permuted_pair,
+                                                             int32_t* __restrict__ unpermute)
+{
+    __shared__ int run[MOE_MAX_EXPERTS];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) run[e] = base[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int p0 = blockIdx.x * kChunk;
+    const int p1 = min(P, p0 + kChunk);
+    for (int pb = p0; pb < p1; pb += 64) {
+        const int p = pb + lane;
+        const bool valid = p < p1;
+        const int e = valid ? clamp_id(ids[p], E) : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(valid && bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lower);
+        const int r0 = valid ? run[e] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            const int row = r0 + rank;
+            permuted_pair[row] = p;
+            unpermute[p] = row;
+            if ((peers >> lane) == 1ull)  // highest lane of its peer group
+                run[e] = r0 + __popcll(peers);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+}  // namespace
+
+size_t permute_scratch_bytes(int T, int k, int E)
+{
+    const size_t P = (size_t)T * k;
+    const size_t nchunks = (P + kChunk - 1) / kChunk;
+    return nchunks * (size_t)E * sizeof(int32_t);
+}
+
+moe_status launch_permute(const int32_t* ids, int T, int k, int E, int n_shared,
+                          int32_t* offsets, int32_t* permuted_pair, int32_t* unpermute,
+                          void* ws, hipStream_t s)
+{
+    const int P = T * k;
+    const int nchunks = (P + kChunk - 1) / kChunk;
+    int32_t* counts = static_cast<int32_t*>(ws);
+    {
+        TimedLaunch tl(MOE_KID_PERMUTE_COUNT, s);
+        hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(256), 0, s, ids, P, E,
+                           counts);
+    }
+    moe_status st = launch_status("permute_count_kernel");
+    if (st != MOE_OK) return st;
+    {
+        TimedLaunch tl(MOE_KID_PERMUTE_SCAN, s);
+        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, counts, nchunks, T, P,
+                           E, n_shared, offsets);
+    }
+    st = launch_status("permute_scan_kernel");
+    if (st != MOE_OK) return st;
+    {
+        TimedLaunch tl(MOE_KID_PERMUTE_SCATTER, s);
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(64), 0, s, ids, P, E,
+                           counts, permuted_pair, unpermute);
+    }
+    return launch_status("permute_scatter_kernel");
+}
+
+}  // namespace moe

@@ -1,0 +1,228 @@
+// moe_route kernel: one 64-lane wavefront per token.
+//
+// Methods (TensorRT-LLM page "MoE 层前向执行", sections "路由方法枚举" and
+// "DeepSeek-V3 的 noaux_tc"; vLLM page, section "FusedTopKRouter"):
+//   Default            softmax over all E, keep top-k (optionally renormalised)
+//   Renormalize        top-k, then softmax over the k kept logits
+//   RenormalizeNaive   softmax, top-k, renormalise (same values as above)
+//   DeepSeekV3         sigmoid scores; bias added for selection only; group
+//                      score = sum of the group's two best biased keys; keep
+//                      topk_group groups; top-k experts among them; weights
+//                      = unbiased sigmoid / (sum + 1e-20) * scaling.
+//
+// Layout: lane l owns experts l, l+64, l+128, l+192 (E <= 256).  Selection
+// keys are packed into one 64-bit integer (order-preserving fp32 bits, then
+// the inverted expert index) so that a single wave-wide max finds the best
+// key with ties going to the lower index; k rounds of that give the ids in
+// selection order.  Group scores and group ranks go through LDS.
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;  // tokens per 256-thread block
+
+__device__ __forceinline__ uint32_t ordered_bits(float v)
+{
+    v = v + 0.0f;  // -0 and +0 compare equal: make them the same key
+    uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+__device__ __forceinline__ uint64_t pack_key(float v, int e)
+{
+    return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// fl32 of the fp64 sigmoid: the fp32 key both sides of a parity check agree on.
+__device__ __forceinline__ float sigmoid_key(float l)
+{
+#pragma clang fp contract(off)
+    double d = 1.0 / (1.0 + exp(-(double)l));
+    return (float)d;
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
+                                                    int E, int method, int k, int n_group,
+                                                    int topk_group,
+                                                    const float* __restrict__ bias,
+                                                    float scaling, unsigned flags,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ scales)
+{
+#pragma clang fp contract(off)
+    __shared__ float s_sig[kWaves][256];
+    __shared__ float s_key[kWaves][256];
+    __shared__ float s_gs[kWaves][128];
+    __shared__ int s_gsel[kWaves][128];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kWaves + wave;
+    const bool active = t < T;
+    const bool dsv3 = method == MOE_ROUTE_DEEPSEEKV3;
+
+    float logit[4], key[4];
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        valid[i] = active && e < E;
+        logit[i] = valid[i] ? logits[(size_t)t * E + e] : 0.0f;
+        key[i] = logit[i];
+    }
+
+    if (dsv3) {
+        const int gsz = E / n_group;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (valid[i]) {
+                const float sg = sigmoid_key(logit[i]);
+                key[i] = sg + (bias ? bias[e] : 0.0f);  // one fp32 add
+                s_sig[wave][e] = sg;
+                s_key[wave][e] = key[i];
+            }
+        }
+        __syncthreads();
+        // group score: sum of the two largest biased keys of the group
+        if (active) {
+            for (int g = lane; g < n_group; g += 64) {
+                float b1 = -INFINITY, b2 = -INFINITY;
+                for (int i = 0; i < gsz; ++i) {
+                    const float v = s_key[wave][g * gsz + i];
+                    if (v > b1) {
+                        b2 = b1;
+                        b1 = v;
+                    } else if (v > b2) {
+                        b2 = v;
+                    }
+                }
+                s_gs[wave][g] = b1 + b2;  // one fp32 add
+            }
+        }
+        __syncthreads();
+        // a group is kept when fewer than topk_group groups beat it
+        if (active) {
+            for (int g = lane; g < n_group; g += 64) {
+                const float gs = s_gs[wave][g];
+                int rank = 0;
+                for (int o = 0; o < n_group; ++o) {
+                    const float v = s_gs[wave][o];
+                    rank += (v > gs) || (v == gs && o < g);
+                }
+                s_gsel[wave][g] = rank < topk_group;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (valid[i]) valid[i] = s_gsel[wave][e / gsz] != 0;
+        }
+    }
+    if (!active) return;  // no block-wide barrier below this point
+
+    uint64_t cand[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cand[i] = valid[i] ? pack_key(key[i], lane + 64 * i) : 0ull;
+
+    int sel_id[MOE_MAX_TOPK];
+    float sel_key[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        sel_id[j] = 0;
+        sel_key[j] = 0.0f;
+        if (j < k) {
+            uint64_t best = cand[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) best = cand[i] > best ? cand[i] : best;
+            best = wave_max_u64(best);
+            int e = (int)(0xffffffffu - (uint32_t)best);
+            e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+            sel_id[j] = e;
+            sel_key[j] = from_ordered_bits((uint32_t)(best >> 32));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (cand[i] == best) cand[i] = 0ull;
+        }
+    }
+
+    // weights, in fp64, rounded once
+    double w[MOE_MAX_TOPK];
+    double wsum = 0.0;
+    if (dsv3) {
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+            w[j] = (j < k) ? (double)s_sig[wave][sel_id[j]] : 0.0;
+            wsum += w[j];
+        }
+        wsum += 1e-20;
+    } else {
+        const double m = (double)sel_key[0];
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+            w[j] = (j < k) ? exp((double)sel_key[j] - m) : 0.0;
+            wsum += w[j];
+        }
+        const bool renorm = method != MOE_ROUTE_DEFAULT || (flags & MOE_ROUTE_FLAG_RENORMALIZE);
+        if (!renorm) {
+            // plain softmax probability: divide by the sum over all E experts
+            double z = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane + 64 * i < E) z += exp((double)logit[i] - m);
+            wsum = wave_sum_f64(z);
+        }
+    }
+    const double sc = (double)scaling;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j < k && lane == j) {
+            ids[(size_t)t * k + j] = sel_id[j];
+            scales[(size_t)t * k + j] = (float)(w[j] / wsum * sc);
+        }
+    }
+}
+
+}  // namespace
+
+moe_status launch_route(const float* logits, int T, int E, int method, int k, int n_group,
+                        int topk_group, const float* bias, float scaling, unsigned flags,
+                        int32_t* ids, float* scales, hipStream_t s)
+{
+    const int blocks = (T + kWaves - 1) / kWaves;
+    {
+        TimedLaunch tl(MOE_KID_ROUTE, s);
+        hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(256), 0, s, logits, T, E, method, k,
+                           n_group, topk_group, bias, scaling, flags, ids, scales);
+    }
+    return launch_status("route_kernel");
+}
+
+}  // namespace moe

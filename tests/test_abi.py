@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments on the host (before any
+launch) with the documented status codes."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_07_amd as moe
+from mixture_experts_layer_07_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from mixture_experts_layer_07_amd import build
+        build.build(verbose=False)
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_finalize",
+            "moe_workspace_size", "moe_status_string", "moe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in moe.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "moe.h"\nint main(void){return (int)moe_workspace_size(1,1,1,0,128,128,MOE_BF16)==0;}\n')
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                           "-I", os.path.join(ROOT, "include"), str(src)])
+
+
+def err(L):
+    return L.moe_last_error().decode()
+
+
+def test_route_validation(L):
+    r = lambda *a: L.moe_route(*a)  # noqa: E731
+    p = C.c_void_p(16)  # never dereferenced: validation fails first
+    assert r(p, 4, 8, 0, 9, 1, 1, None, 1.0, 0, p, p, None) == INVALID      # k > E
+    assert "k must be" in err(L)
+    assert r(p, 4, 8, 0, 0, 1, 1, None, 1.0, 0, p, p, None) == INVALID      # k = 0
+    assert r(p, 4, 300, 0, 2, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED  # E > 256
+    assert r(p, 4, 64, 0, 9, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED  # k > 8
+    assert r(p, 4, 8, 3, 2, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED   # Llama4
+    assert r(p, 4, 8, 9, 2, 1, 1, None, 1.0, 0, p, p, None) == INVALID       # unknown method
+    assert r(p, 4, 8, 0, 2, 1, 1, None, 1.0, 2, p, p, None) == INVALID       # unknown flag
+    assert r(p, 4, 8, 0, 2, 1, 1, None, float("inf"), 0, p, p, None) == INVALID
+    assert r(p, -1, 8, 0, 2, 1, 1, None, 1.0, 0, p, p, None) == INVALID      # T < 0
+    assert r(None, 4, 8, 0, 2, 1, 1, None, 1.0, 0, p, p, None) == INVALID    # null logits
+    # DeepSeek-V3 group constraints
+    assert r(p, 4, 256, 2, 8, 3, 1, None, 1.0, 0, p, p, None) == INVALID     # 256 % 3
+    assert r(p, 4, 256, 2, 8, 256, 4, None, 1.0, 0, p, p, None) == INVALID   # group of 1
+    assert r(p, 4, 256, 2, 8, 8, 9, None, 1.0, 0, p, p, None) == INVALID     # topk_group > n_group
+    assert r(p, 4, 16, 2, 8, 4, 1, None, 1.0, 0, p, p, None) == INVALID      # k > kept experts
+    # T = 0 is a no-op even with null buffers
+    assert r(None, 0, 256, 2, 8, 8, 4, None, 2.5, 0, None, None, None) == OK
+
+
+def test_permute_validation(L):
+    p = C.c_void_p(16)
+    assert L.moe_permute(p, 10, 2, 8, 0, p, p, p, None, 0, None) == WORKSPACE
+    assert L.moe_permute(p, 10, 2, 8, 0, p, p, p, p, 3, None) == WORKSPACE
+    assert L.moe_permute(p, 10, 2, 8, -1, p, p, p, p, 1 << 20, None) == INVALID
+    assert L.moe_permute(None, 10, 2, 8, 0, p, p, p, p, 1 << 20, None) == INVALID
+    assert L.moe_permute(p, 10, 9, 8, 0, p, p, p, p, 1 << 20, None) == INVALID
+
+
+def test_expert_ffn_validation(L):
+    p = C.c_void_p(16)
+    f = lambda act, H, I, wdt, s13=p, s2=p, ws=p, wsb=1 << 30: L.moe_expert_ffn(  # noqa: E731
+        p, act, 16, H, I, 2, 8, 0, p, p, p, p, wdt, s13, s2, p, ws, wsb, None)
+    assert f(1, 100, 128, 1) == UNSUPPORTED             # H % 128
+    assert f(1, 128, 96, 1) == UNSUPPORTED              # I % 128
+    assert f(0, 128, 128, 1) == UNSUPPORTED             # fp32 act with bf16 weights
+    assert f(1, 128, 128, 0) == UNSUPPORTED             # bf16 act with fp32 weights
+    assert f(2, 128, 128, 2) == INVALID                 # fp8 activations
+    assert f(1, 128, 128, 2, s13=None) == INVALID       # fp8 needs scales
+    assert f(1, 128, 128, 1, ws=None) == WORKSPACE
+    assert f(1, 128, 128, 1, wsb=16) == WORKSPACE
+    assert f(1, 0, 128, 1) == INVALID
+
+
+def test_finalize_validation(L):
+    p = C.c_void_p(16)
+    assert L.moe_finalize(p, 1, p, p, 4, 2, 100, 0, p, 1, None) == UNSUPPORTED  # H % 8
+    assert L.moe_finalize(p, 2, p, p, 4, 2, 128, 0, p, 1, None) == INVALID      # fp8 rows
+    assert L.moe_finalize(p, 1, p, p, 4, 9, 128, 0, p, 1, None) == UNSUPPORTED  # k > 8
+    assert L.moe_finalize(p, 1, None, p, 4, 2, 128, 0, p, 1, None) == INVALID
+
+
+def test_workspace_size_and_strings(L):
+    f = L.moe_workspace_size
+    a = f(512, 8, 256, 0, 7168, 2048, 1)
+    b = f(8192, 8, 256, 1, 7168, 2048, 1)
+    assert 0 < a < b
+    assert b >= (8192 * 8 + 8192) * 2048 * 2     # holds h in bf16
+    assert f(64, 2, 8, 0, 256, 512, 0) >= 128 * 512 * 4
+    assert f(4, 9, 8, 0, 128, 128, 1) == 0       # invalid: k > E
+    for st in range(5):
+        assert L.moe_status_string(st).decode().startswith("MOE_")
+    assert "unknown" in L.moe_status_string(77).decode()
+
+
+def test_timing_api_without_launches(L):
+    assert L.moe_timing_enable(1) == OK
+    t = binding.kernel_times(reset=True)
+    assert set(t) == set(binding.KERNEL_IDS) and all(v == (0.0, 0) for v in t.values())
+    assert L.moe_timing_enable(0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
