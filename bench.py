@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one pass of the whole path (route -> permute -> FC1+SwiGLU -> FC2 ->
+finalize) over one batch of the synthetic workload, inputs already resident in
+HBM.  Prints ONE JSON line on stdout (details go to stderr):
+
+  value      whole-job tokens/s of the headline workload (DeepSeek-V3-shaped
+             prefill, T=8192, H=7168, 256 routed experts + 1 shared, top-8)
+  roofline   the dominant kernel (FC1 grouped GEMM): algorithmic bytes/FLOPs
+             per launch / its mean launch duration from HIP events recorded on
+             the launch stream during the timed steps
+  decode     the same figures for the DeepSeek-V3-shaped decode batch (T=512)
+  cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
+             workload on this host's cores (a reported baseline, not a target)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm": 8000.0, "bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # GB/s, TFLOP/s
+DOMINANT = "fc1"
+KERNEL_SOURCE = os.path.join(ROOT, "mixture_experts_layer_07_amd", "csrc", "ffn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def fc_work(w, touched_groups, which):
+    """Algorithmic FLOPs and HBM bytes of one FC1 or FC2 launch.
+
+    FC1: 2*R*H*(2I) FLOPs; reads every touched group's w13 (2I*H weights, +
+    fp8 scales), each token's activation row once, writes h (R*I).
+    FC2: 2*R*I*H FLOPs; reads touched w2 (H*I) and h, writes fc2_out (R*H).
+    """
+    wsz = {"f32": 4, "bf16": 2, "fp8": 1}[w.wdt]
+    asz = 4 if w.act == "f32" else 2
+    R, H, I, T = w.R, w.H, w.I, w.T
+    sc = 4.0 / (128 * 128) if w.wdt == "fp8" else 0.0
+    if which == "fc1":
+        flops = 2.0 * R * H * 2 * I
+        nbytes = touched_groups * 2 * I * H * (wsz + sc) + T * H * asz + R * I * asz
+    else:
+        flops = 2.0 * R * I * H
+        nbytes = touched_groups * H * I * (wsz + sc) + R * I * asz + R * H * asz
+    return flops, nbytes
+
+
+def roofline(w, touched, ms_per_launch, which=DOMINANT, traffic=None):
+    flops, nbytes = fc_work(w, touched, which)
+    peak_f = PEAK["f32" if w.act == "f32" else "bf16"]
+    t_f = flops / (peak_f * 1e12)
+    t_b = nbytes / (PEAK["hbm"] * 1e9)
+    s = ms_per_launch * 1e-3
+    if t_f >= t_b:
+        ach, peak, unit, bound = flops / s / 1e12, peak_f, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = nbytes / s / 1e9, PEAK["hbm"], "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic,
+            "kernel": f"grouped_gemm_kernel ({which})", "ms_per_launch": round(ms_per_launch, 4),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "mfma_frac": round(flops / s / 1e12 / peak_f, 4),
+            "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
+
+
+def load_traffic(workload):
+    """HBM bytes per FC1 launch from the committed rocprofv3 counter summary,
+    or None when the summary is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, device):
+    import torch
+    import mixture_experts_layer_07_amd as moe
+    from mixture_experts_layer_07_amd import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    t0 = time.time()
+    inp = wl.make_inputs(w, 0, device)
+    layer = moe.layer_for_workload(w, device)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+
+    def step():
+        return layer(inp["x"], inp["logits"], inp["w13"], inp["w2"], inp["bias"],
+                     inp["w13_scale"], inp["w2_scale"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.timing_enable(True)
+    moe.kernel_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kt = moe.kernel_times(reset=True)
+    moe.timing_enable(False)
+    cnt = torch.bincount(layer.ids.flatten().long(), minlength=w.E).cpu()
+    touched = int((cnt > 0).sum()) + w.n_shared
+    ms = elapsed * 1e3 / steps
+    per_kernel = {k: round(v[0] / max(v[1], 1), 4) for k, v in kt.items()}
+    log(f"[bench] {name}: {ms:.3f} ms/step, per-kernel ms {per_kernel}")
+    log(f"[bench] {name}: rows per expert min {int(cnt.min())} median "
+        f"{int(cnt.median())} max {int(cnt.max())}, empty experts {int((cnt == 0).sum())}")
+    return dict(w=w, inp=inp, layer=layer, ms=ms, per_kernel=per_kernel, touched=touched,
+                counts=cnt)
+
+
+def cpu_baseline(res, seconds):
+    """Time the CPU oracle on a bounded token sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    w, inp, layer = res["w"], res["inp"], res["layer"]
+    host = lambda t: None if t is None else t.detach().cpu()  # noqa: E731
+    x, logits, bias = host(inp["x"]), host(inp["logits"]), host(inp["bias"])
+    t0 = time.perf_counter()
+    ids, sc, _ = oracle.route(logits, w.k, w.method, w.n_group, w.topk_group, bias, w.scaling,
+                              bool(w.flags & 1))
+    oracle.permute(ids, w.E, w.n_shared)
+    t_route = time.perf_counter() - t0
+    W = oracle.Weights(host(inp["w13"]), host(inp["w2"]), w.wdt, host(inp["w13_scale"]),
+                       host(inp["w2_scale"]))
+    threads = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.T).astype(np.int32)
+    done, t_ffn, batch = 0, 0.0, threads
+    while done < w.T and t_ffn < seconds:
+        toks = order[done:done + batch]
+        t0 = time.perf_counter()
+        oracle.layer_tokens(W, x, w.act, w.T, w.k, w.E, w.n_shared, ids, sc, toks)
+        t_ffn += time.perf_counter() - t0
+        done += len(toks)
+        batch = threads * 2
+    est = t_route + t_ffn * w.T / done
+    return {"value": round(w.T / est, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{w.name}: routing + permute of all {w.T} tokens ({t_route:.2f}s), "
+                       f"expert FFN + weighted sum of {done} random tokens ({t_ffn:.1f}s), "
+                       f"scaled to {w.T} tokens; fp64, OpenMP over tokens")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--decode-workload", default="dsv3_decode")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the layer keeps all experts on one device "
+              f"and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    main_res = run_workload(args.workload, args.steps, args.warmup, dev)
+    w = main_res["w"]
+    traffic = load_traffic(args.workload)
+    rl = roofline(w, main_res["touched"], main_res["per_kernel"][DOMINANT], traffic=traffic)
+    out = {
+        "metric": "MoE layer tokens/s + grouped-GEMM %MFMA / %HBM peak, DSV3 shapes T=512/8192",
+        "value": round(w.T / (main_res["ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E}+{w.n_shared} shared "
+                               f"I={w.I} top-{w.k}, route method {w.method}, "
+                               f"{w.act} activations, {w.wdt} weights",
+                   "global_batch": w.T, "parallelism": "single GPU, all experts local"},
+        "roofline": rl,
+        "per_kernel_ms": main_res["per_kernel"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
+        log(f"[bench] cpu baseline {out['cpu_baseline']}")
+    del main_res
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        d = run_workload(args.decode_workload, args.steps, args.warmup, dev)
+        dw = d["w"]
+        out["decode"] = {
+            "workload": f"{dw.name}: T={dw.T} H={dw.H} E={dw.E} I={dw.I} top-{dw.k}",
+            "value": round(dw.T / (d["ms"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(d["ms"], 4),
+            "roofline": roofline(dw, d["touched"], d["per_kernel"][DOMINANT],
+                                 traffic=load_traffic(args.decode_workload)),
+            "roofline_fc2": roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2"),
+            "per_kernel_ms": d["per_kernel"],
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
