@@ -60,19 +60,23 @@ def fc_work(w, touched_groups, which):
     return flops, nbytes
 
 
-def roofline(w, touched, ms_per_launch, which=DOMINANT, traffic=None):
+def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=None):
+    """Roofline of one grouped GEMM per step.  A grouped GEMM is issued as one
+    launch per row class of groups (tile shape); its time per step is the sum
+    of those launches, and the algorithmic work is that of the whole GEMM."""
     flops, nbytes = fc_work(w, touched, which)
     peak_f = PEAK["f32" if w.act == "f32" else "bf16"]
     t_f = flops / (peak_f * 1e12)
     t_b = nbytes / (PEAK["hbm"] * 1e9)
-    s = ms_per_launch * 1e-3
+    s = ms_per_step * 1e-3
     if t_f >= t_b:
         ach, peak, unit, bound = flops / s / 1e12, peak_f, "TFLOP/s", "mfma"
     else:
         ach, peak, unit, bound = nbytes / s / 1e9, PEAK["hbm"], "GB/s", "hbm"
     return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
             "frac": round(ach / peak, 4), "traffic": traffic,
-            "kernel": f"grouped_gemm_kernel ({which})", "ms_per_launch": round(ms_per_launch, 4),
+            "kernel": f"grouped GEMM {which.upper()} (row-class launches per step: {launches})",
+            "ms_per_step": round(ms_per_step, 4),
             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
             "mfma_frac": round(flops / s / 1e12 / peak_f, 4),
             "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
@@ -123,12 +127,14 @@ def run_workload(name, steps, warmup, device):
     cnt = torch.bincount(layer.ids.flatten().long(), minlength=w.E).cpu()
     touched = int((cnt > 0).sum()) + w.n_shared
     ms = elapsed * 1e3 / steps
-    per_kernel = {k: round(v[0] / max(v[1], 1), 4) for k, v in kt.items()}
-    log(f"[bench] {name}: {ms:.3f} ms/step, per-kernel ms {per_kernel}")
+    # per step: a grouped GEMM is one launch per row class of groups (tile shape)
+    per_kernel = {k: round(v[0] / steps, 4) for k, v in kt.items()}
+    launches = {k: v[1] // steps for k, v in kt.items()}
+    log(f"[bench] {name}: {ms:.3f} ms/step, per-kernel ms per step {per_kernel}, launches per step {launches}")
     log(f"[bench] {name}: rows per expert min {int(cnt.min())} median "
         f"{int(cnt.median())} max {int(cnt.max())}, empty experts {int((cnt == 0).sum())}")
     return dict(w=w, inp=inp, layer=layer, ms=ms, per_kernel=per_kernel, touched=touched,
-                counts=cnt)
+                counts=cnt, launches=launches)
 
 
 def cpu_baseline(res, seconds):
@@ -188,7 +194,8 @@ def main():
     main_res = run_workload(args.workload, args.steps, args.warmup, dev)
     w = main_res["w"]
     traffic = load_traffic(args.workload)
-    rl = roofline(w, main_res["touched"], main_res["per_kernel"][DOMINANT], traffic=traffic)
+    rl = roofline(w, main_res["touched"], main_res["per_kernel"][DOMINANT], traffic=traffic,
+                  launches=main_res["launches"][DOMINANT])
     out = {
         "metric": "MoE layer tokens/s + grouped-GEMM %MFMA / %HBM peak, DSV3 shapes T=512/8192",
         "value": round(w.T / (main_res["ms"] * 1e-3), 1),
@@ -222,8 +229,10 @@ def main():
             "value": round(dw.T / (d["ms"] * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(d["ms"], 4),
             "roofline": roofline(dw, d["touched"], d["per_kernel"][DOMINANT],
-                                 traffic=load_traffic(args.decode_workload)),
-            "roofline_fc2": roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2"),
+                                 traffic=load_traffic(args.decode_workload),
+                                 launches=d["launches"][DOMINANT]),
+            "roofline_fc2": roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2",
+                                     launches=d["launches"]["fc2"]),
             "per_kernel_ms": d["per_kernel"],
         }
     print(json.dumps(out), flush=True)

@@ -21,7 +21,7 @@
 //
 // Tile engine.  Both operands are K-contiguous (activation rows and weight
 // rows), staged through LDS in 128-byte K slices (64 bf16 or 32 fp32 values
-// per row) with a 16-byte pad per row (conflict-free 16-byte fragment reads).
+// per row) whose 16-byte chunks are XOR-swizzled by row (conflict-free).
 // Double-buffered LDS with one barrier per K slice; the next slice's global
 // loads are in flight while MFMAs run on the current one.
 //   bf16:  v_mfma_f32_16x16x32_bf16; a lane feeds 8 consecutive K values of one
@@ -60,15 +60,22 @@ struct FfnArgs {
     int N;                     // GEMM output columns (FC1: 2I, FC2: H)
     int K;                     // reduction length (FC1: H, FC2: I)
     int out_ld;                // FC1: I, FC2: H
+    int lo_rows, hi_rows;      // this launch serves groups with lo <= rows < hi
 };
 
 constexpr int kRowBytes = 128;                 // K slice per row, bytes
-constexpr int kLdsStride = kRowBytes + 16;     // padded LDS row
+constexpr int kLdsStride = kRowBytes;          // LDS row (no pad: XOR-swizzled chunks)
+
+// LDS byte offset of 16-byte chunk `kc` (0..7) of staged row `row`.  The chunk
+// index is XORed with row % 8: measured on gfx950, this makes both the
+// fragment reads (16 rows x 4 chunks per ds_read_b128) and the staging writes
+// (8 lanes per row) free of bank conflicts, where a padded 144-byte row is not.
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * kLdsStride + ((kc ^ (row & 7)) << 4); }
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 64;
 
-template <class AT, class WT, int BM_, int BN_, int WM_, int WN_>
+template <class AT, class WT, int BM_, int BN_, int WM_, int WN_, int GM_ = 1>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_;
     static constexpr int NT = WM * WN * 64;
     static constexpr bool F32 = sizeof(AT) == 4;           // fp32 compute
     static constexpr bool FP8 = sizeof(WT) == 1;
@@ -114,6 +121,15 @@ __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
 
+// 16-byte load through the global address space.  The tile pointers live in
+// a by-value struct and loop-carried registers, where the compiler cannot infer
+// the address space and would emit flat loads, which also count against the
+// LDS wait counter and so serialise the global latency with LDS traffic.
+__device__ __forceinline__ u32x4_t ldg16(const char* p)
+{
+    return *(const __attribute__((address_space(1))) u32x4_t*)(p);
+}
+
 // Global -> registers: the A and B chunks of K slice kt.
 template <class C, class WT>
 __device__ __forceinline__ void gload(u32x4_t (&ra)[C::A_CH], u32x4_t (&rb)[C::B_CH],
@@ -125,9 +141,9 @@ __device__ __forceinline__ void gload(u32x4_t (&ra)[C::A_CH], u32x4_t (&rb)[C::B
     const size_t kb = (size_t)kt * C::BK * sizeof(WT);   // W bytes
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i)
-        ra[i] = a_ok[i] ? *reinterpret_cast<const u32x4_t*>(a_ptr[i] + ka) : u32x4_t{0u, 0u, 0u, 0u};
+        ra[i] = a_ok[i] ? ldg16(a_ptr[i] + ka) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(b_ptr[i] + kb);
+    for (int i = 0; i < C::B_CH; ++i) rb[i] = ldg16(b_ptr[i] + kb);
 }
 
 // Registers -> LDS buffer `buf` (fp8 weights widened to bf16 on the way).
@@ -140,7 +156,7 @@ __device__ __forceinline__ void lstore(char* lds, const u32x4_t (&ra)[C::A_CH],
 #pragma unroll
     for (int i = 0; i < C::A_CH; ++i) {
         const int c = tid + i * C::NT;
-        *reinterpret_cast<u32x4_t*>(la + (c >> 3) * kLdsStride + (c & 7) * 16) = ra[i];
+        *reinterpret_cast<u32x4_t*>(la + lds_off(c >> 3, c & 7)) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < C::B_CH; ++i) {
@@ -152,11 +168,82 @@ __device__ __forceinline__ void lstore(char* lds, const u32x4_t (&ra)[C::A_CH],
             lo4.z = fp8x2_to_bf16x2<false>(rb[i].y); lo4.w = fp8x2_to_bf16x2<true>(rb[i].y);
             hi4.x = fp8x2_to_bf16x2<false>(rb[i].z); hi4.y = fp8x2_to_bf16x2<true>(rb[i].z);
             hi4.z = fp8x2_to_bf16x2<false>(rb[i].w); hi4.w = fp8x2_to_bf16x2<true>(rb[i].w);
-            *reinterpret_cast<u32x4_t*>(lb + j * kLdsStride + q * 32) = lo4;
-            *reinterpret_cast<u32x4_t*>(lb + j * kLdsStride + q * 32 + 16) = hi4;
+            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, 2 * q)) = lo4;
+            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, 2 * q + 1)) = hi4;
         } else {
-            *reinterpret_cast<u32x4_t*>(lb + j * kLdsStride + q * 16) = rb[i];
+            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, q)) = rb[i];
         }
+    }
+}
+
+// Tile of the flattened work list, decoded.
+struct TileInfo {
+    int g, row0, nrows, m0, nt;
+};
+
+template <class C>
+__device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_off, const int* s_tile0,
+                                                int G, int ntiles_n)
+{
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {  // last g with s_tile0[g] <= tile
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    TileInfo ti;
+    ti.g = lo;
+    ti.row0 = s_off[lo];
+    ti.nrows = s_off[lo + 1] - ti.row0;
+    const int mtiles = (ti.nrows + C::BM - 1) / C::BM;
+    // group-M order: runs of GM M-tiles share one N-tile, so a contiguous slice
+    // of the list reuses both operands (A across N-tiles, B across M-tiles)
+    const int local = tile - s_tile0[lo];
+    const int band = local / (C::GM * ntiles_n);
+    const int first_m = band * C::GM;
+    const int gm = min(mtiles - first_m, C::GM);
+    const int r = local - band * C::GM * ntiles_n;
+    ti.m0 = (first_m + r % gm) * C::BM;
+    ti.nt = r / gm;
+    return ti;
+}
+
+// Per-thread global source pointers of a tile's A rows and B (weight) rows.
+template <class AT, class WT, int MODE, class C>
+__device__ __forceinline__ void tile_pointers(const FfnArgs& a, const TileInfo& ti, int tid,
+                                              const char* (&a_ptr)[C::A_CH], bool (&a_ok)[C::A_CH],
+                                              const char* (&b_ptr)[C::B_CH])
+{
+    const size_t a_ld = (size_t)a.K * sizeof(AT);
+    const size_t w_ld = (size_t)a.K * sizeof(WT);
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i) {
+        const int c = tid + i * C::NT;
+        const int rr = ti.m0 + (c >> 3);
+        a_ok[i] = rr < ti.nrows;
+        long src = 0;
+        if (a_ok[i]) {
+            if (MODE == FC1) {
+                int tok = (ti.g < a.E) ? a.permuted_pair[ti.row0 + rr] / a.k : rr;
+                src = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            } else {
+                src = ti.row0 + rr;
+            }
+        }
+        a_ptr[i] = a.a_src + (size_t)src * a_ld + (size_t)(c & 7) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i) {
+        const int c = tid + i * C::NT;
+        const int j = c / C::B_GCH;  // staged B row
+        int wrow;
+        if (MODE == FC1) {
+            const int blk = j >> 4, pair = blk >> 1;
+            const int col = ti.nt * (C::BN / 2) + pair * 16 + (j & 15);
+            wrow = (blk & 1) ? a.I + col : col;
+        } else {
+            wrow = min(ti.nt * C::BN + j, a.N - 1);  // partial last N-tile: rows past N unused
+        }
+        b_ptr[i] = a.w + ((size_t)ti.g * a.N + wrow) * w_ld + (size_t)(c % C::B_GCH) * 16;
     }
 }
 
@@ -173,20 +260,22 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
     const int wave = tid >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int G = a.G;
-    const int NTILES_N = (MODE == FC1) ? a.N / C::BN : a.N / C::BN;
+    // FC2's N (= H) is a multiple of 128 only: the last N-tile may be partial
+    const int ntiles_n = (a.N + C::BN - 1) / C::BN;
 
-    // ---- flattened tile list: group g owns tiles [s_tile0[g], s_tile0[g+1])
+    // ---- flattened tile list of the groups in this launch's row class
+    //      [a.lo_rows, a.hi_rows): group g owns tiles [s_tile0[g], s_tile0[g+1])
     for (int g = tid; g <= G; g += C::NT) s_off[g] = a.offsets[g];
     __syncthreads();
     if (wave == 0) {
-        // per lane, a contiguous run of groups; wave-wide exclusive scan
-        const int per = (G + 63) / 64;
+        const int per = (G + 63) / 64;  // a contiguous run of groups per lane
         const int g0 = lane * per, g1 = min(G, g0 + per);
+        auto ntiles = [&](int g) {
+            const int n = s_off[g + 1] - s_off[g];
+            return (n >= a.lo_rows && n < a.hi_rows && n > 0) ? (n + C::BM - 1) / C::BM * ntiles_n : 0;
+        };
         int sum = 0;
-        for (int g = g0; g < g1; ++g) {
-            const int n = max(0, s_off[g + 1] - s_off[g]);
-            sum += (n + C::BM - 1) / C::BM * NTILES_N;
-        }
+        for (int g = g0; g < g1; ++g) sum += ntiles(g);
         int incl = sum;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -196,8 +285,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
         int run = incl - sum;
         for (int g = g0; g < g1; ++g) {
             s_tile0[g] = run;
-            const int n = max(0, s_off[g + 1] - s_off[g]);
-            run += (n + C::BM - 1) / C::BM * NTILES_N;
+            run += ntiles(g);
         }
         if (lane == 63) s_tile0[G] = incl;
     }
@@ -207,67 +295,27 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
     const int nb = gridDim.x;
     const bool xcd_map = (nb % 8) == 0;
     const int slot = xcd_map ? (blockIdx.x >> 3) + (blockIdx.x & 7) * (nb >> 3) : blockIdx.x;
+    int tile = slot;
+    if (tile >= total) return;
 
     const int nk = a.K / C::BK;
-    const size_t a_ld = (size_t)((MODE == FC1) ? a.K : a.K) * sizeof(AT);  // A row bytes
-    const size_t w_ld = (size_t)a.K * sizeof(WT);                          // W row bytes
+    const char* a_ptr[C::A_CH];
+    bool a_ok[C::A_CH];
+    const char* b_ptr[C::B_CH];
+    u32x4_t ra[C::A_CH], rb[C::B_CH];
 
-    for (int tile = slot; tile < total; tile += nb) {
-        // ---- decode tile -> (g, nt, mt)
-        int lo = 0, hi = G - 1;
-        while (lo < hi) {  // last g with s_tile0[g] <= tile
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tile0[mid] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int g = lo;
-        const int row0 = s_off[g];
-        const int nrows = s_off[g + 1] - row0;
-        const int mtiles = (nrows + C::BM - 1) / C::BM;
-        const int local = tile - s_tile0[g];
-        const int nt = local / mtiles;
-        const int mt = local - nt * mtiles;
-        const int m0 = mt * C::BM;
+    TileInfo cur = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
+    tile_pointers<AT, WT, MODE, C>(a, cur, tid, a_ptr, a_ok, b_ptr);
+    gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, 0);
+    lstore<C>(lds, ra, rb, tid, 0);
+    __syncthreads();
+    int buf = 0;
 
-        // ---- per-thread global source rows
-        const char* a_ptr[C::A_CH];
-        bool a_ok[C::A_CH];
-#pragma unroll
-        for (int i = 0; i < C::A_CH; ++i) {
-            const int c = tid + i * C::NT;
-            const int r = c >> 3;
-            const int rr = m0 + r;
-            a_ok[i] = rr < nrows;
-            long src;
-            if (MODE == FC1) {
-                int tok = 0;
-                if (a_ok[i]) {
-                    tok = (g < a.E) ? a.permuted_pair[row0 + rr] / a.k : rr;
-                    tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
-                }
-                src = tok;
-            } else {
-                src = a_ok[i] ? row0 + rr : 0;
-            }
-            a_ptr[i] = a.a_src + (size_t)src * a_ld + (size_t)(c & 7) * 16;
-        }
-        const char* b_ptr[C::B_CH];
-#pragma unroll
-        for (int i = 0; i < C::B_CH; ++i) {
-            const int c = tid + i * C::NT;
-            const int j = c / C::B_GCH;  // B tile row
-            int wrow;
-            if (MODE == FC1) {
-                const int blk = j >> 4, pair = blk >> 1;
-                const int col = nt * (C::BN / 2) + pair * 16 + (j & 15);
-                wrow = (blk & 1) ? a.I + col : col;
-            } else {
-                wrow = nt * C::BN + j;
-            }
-            b_ptr[i] = a.w + ((size_t)g * a.N + wrow) * w_ld + (size_t)(c % C::B_GCH) * 16;
-        }
+    while (true) {
+        const int next_tile = tile + nb;
+        const bool has_next = next_tile < total;
+        TileInfo nxt = cur;
 
-        // ---- K loop
-        u32x4_t ra[C::A_CH], rb[C::B_CH];
         f32x4_t acc[C::MI][C::NI];
         f32x4_t part[C::FP8 ? C::MI : 1][C::FP8 ? C::NI : 1];
 #pragma unroll
@@ -278,15 +326,22 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) part[C::FP8 ? mi : 0][C::FP8 ? ni : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int ni = 0; ni < C::NI; ++ni)
+                    part[C::FP8 ? mi : 0][C::FP8 ? ni : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
 
-        gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, 0);
-        lstore<C>(lds, ra, rb, tid, 0);
-        __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, kt + 1);
+            // issue the next slice's loads: this tile's, or the next tile's first
+            bool staged = true;
+            if (kt + 1 < nk) {
+                gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, kt + 1);
+            } else if (has_next) {
+                nxt = decode_tile<C>(next_tile, s_off, s_tile0, G, ntiles_n);
+                tile_pointers<AT, WT, MODE, C>(a, nxt, tid, a_ptr, a_ok, b_ptr);
+                gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, 0);
+            } else {
+                staged = false;
+            }
             const char* la = lds + buf * (C::LDS_A + C::LDS_B);
             const char* lb = la + C::LDS_A;
 #pragma unroll
@@ -295,11 +350,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
                     fa[mi] = *reinterpret_cast<const u32x4_t*>(
-                        la + (wm * C::WTM + mi * 16 + (lane & 15)) * kLdsStride + ks * 64 + (lane >> 4) * 16);
+                        la + lds_off(wm * C::WTM + mi * 16 + (lane & 15), ks * 4 + (lane >> 4)));
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni)
                     fb[ni] = *reinterpret_cast<const u32x4_t*>(
-                        lb + (wn * C::WTN + ni * 16 + (lane & 15)) * kLdsStride + ks * 64 + (lane >> 4) * 16);
+                        lb + lds_off(wn * C::WTN + ni * 16 + (lane & 15), ks * 4 + (lane >> 4)));
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -312,7 +367,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
                     }
             }
             if (C::FP8 && ((kt + 1) * C::BK) % 128 == 0) {
-                // end of a 128-wide K block: acc += scale * partial
+                // end of a 128-wide K block: acc += block scale * partial
                 const int kb = (kt * C::BK) / 128;
                 const int sk = a.K / 128;
 #pragma unroll
@@ -321,12 +376,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
                     int wrow;
                     if (MODE == FC1) {
                         const int blk = j >> 4, pair = blk >> 1;
-                        const int col = nt * (C::BN / 2) + pair * 16;
+                        const int col = cur.nt * (C::BN / 2) + pair * 16;
                         wrow = (blk & 1) ? a.I + col : col;
                     } else {
-                        wrow = nt * C::BN + j;
+                        wrow = min(cur.nt * C::BN + j, a.N - 1);
                     }
-                    const float s = a.wscale[((size_t)g * (a.N / 128) + wrow / 128) * sk + kb];
+                    const float s = a.wscale[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kb];
 #pragma unroll
                     for (int mi = 0; mi < C::MI; ++mi) {
                         acc[mi][ni] += s * part[C::FP8 ? mi : 0][C::FP8 ? ni : 0];
@@ -334,11 +389,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
                     }
                 }
             }
-            if (kt + 1 < nk) lstore<C>(lds, ra, rb, tid, buf ^ 1);
+            if (staged) lstore<C>(lds, ra, rb, tid, buf ^ 1);
             __syncthreads();
+            buf ^= 1;
         }
 
-        // ---- epilogue
+        // ---- epilogue (registers -> global; the next tile's first slice is in LDS)
         AT* out = reinterpret_cast<AT*>(a.out);
         if (MODE == FC1) {
 #pragma unroll
@@ -346,15 +402,16 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 #pragma unroll
                 for (int q = 0; q < C::NI / 2; ++q) {
                     const int pair = (wn * C::WTN) / 32 + q;
-                    const int col = nt * (C::BN / 2) + pair * 16 + (lane & 15);
+                    const int col = cur.nt * (C::BN / 2) + pair * 16 + (lane & 15);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < nrows) {
+                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < cur.nrows) {
                             const float gt = acc[mi][2 * q][i];
                             const float up = acc[mi][2 * q + 1][i];
-                            const float hv = gt / (1.0f + expf(-gt)) * up;
-                            store_out(out + (size_t)(row0 + rr) * a.out_ld + col, hv);
+                            // silu(g) * u; v_rcp_f32 (1 ulp) instead of an IEEE divide
+                            const float hv = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
+                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, hv);
                         }
                     }
                 }
@@ -363,23 +420,281 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
-                    const int col = nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
+                    const int col = cur.nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < nrows) store_out(out + (size_t)(row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
+                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < cur.nrows && col < a.N)
+                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
                     }
                 }
         }
+        if (!has_next) break;
+        tile = next_tile;
+        cur = nxt;
     }
 }
 
-struct DevInfo {
-    int cus = 0;
+// ---------------------------------------------------------------------------
+// bf16 x bf16 tile engine with direct global->LDS loads.
+//
+// Each stage is a 64-byte K slice (32 bf16) of BM activation rows and BN weight
+// rows, written straight into LDS by global_load_lds_dwordx4: one instruction
+// moves 1 KB = 16 rows x 64 B, lane l landing at byte 16*l of it.  The ring
+// holds S stages, so loads run S-1 slices ahead of the MFMAs without holding
+// anything in VGPRs; one barrier per slice.  Chunk c of row r is stored at
+// chunk c ^ ((r >> 1) & 3) (measured conflict-free on gfx950 for both the
+// 16-row x 4-chunk fragment reads and the DMA writes).
+template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int NW = WM * WN;
+    static constexpr int BK = 32;                          // K per stage
+    static constexpr int ROWB = 64;                        // bytes per staged row
+    static constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
+    static constexpr int NINS = (BM + BN) / 16;            // 1 KB DMA ops per stage
+    static constexpr int IPW = (NINS + NW - 1) / NW;       // max per wave
+    static constexpr int IPW_MIN = NINS / NW;              // min per wave
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int MI = WTM / 16, NI = WTN / 16;
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && WTM % 16 == 0 && WTN % 32 == 0, "tile");
+    static_assert(IPW_MIN >= 1, "every wave issues loads");
 };
 
+__device__ __forceinline__ int dma_off(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane global->LDS transfer into the 1 KB at LDS byte address
+// `lds_addr` (wave-uniform).  Written as inline asm on purpose: the compiler's
+// own tracking of LDS DMA inserts a full vmcnt(0) wait before every later LDS
+// read, which would drain the ring each slice; the kernel instead waits for
+// exactly the stage it needs (wait_vmcnt) before the barrier that publishes it.
+// M0 is reserved by the compiler and used by nothing else in this kernel.
+__device__ __forceinline__ void dma16(unsigned lds_addr, const char* src)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+}
+
+// Barrier that orders LDS only (s_waitcnt lgkmcnt(0) + s_barrier): unlike
+// __syncthreads() it does not wait for the DMA loads still in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int MODE, class C>
+__global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[C::S * C::STAGE];
+    __shared__ int s_off[kMaxGroups + 1];
+    __shared__ int s_tile0[kMaxGroups + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int G = a.G;
+    const int ntiles_n = (a.N + C::BN - 1) / C::BN;
+
+    for (int g = tid; g <= G; g += C::NT) s_off[g] = a.offsets[g];
+    __syncthreads();
+    if (wave == 0) {
+        const int per = (G + 63) / 64;
+        const int g0 = lane * per, g1 = min(G, g0 + per);
+        auto ntiles = [&](int g) {
+            const int n = s_off[g + 1] - s_off[g];
+            return (n >= a.lo_rows && n < a.hi_rows && n > 0) ? (n + C::BM - 1) / C::BM * ntiles_n : 0;
+        };
+        int sum = 0;
+        for (int g = g0; g < g1; ++g) sum += ntiles(g);
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        int run = incl - sum;
+        for (int g = g0; g < g1; ++g) {
+            s_tile0[g] = run;
+            run += ntiles(g);
+        }
+        if (lane == 63) s_tile0[G] = incl;
+    }
+    __syncthreads();
+    const int total = s_tile0[G];
+    const int nb = gridDim.x;
+    const bool xcd_map = (nb % 8) == 0;
+    const int slot = xcd_map ? (blockIdx.x >> 3) + (blockIdx.x & 7) * (nb >> 3) : blockIdx.x;
+    const int nk = a.K / C::BK;
+    const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * 2;
+
+    // this lane's row within a DMA op and the logical chunk it fetches
+    const int lrow = lane >> 2;
+    const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+
+    for (int tile = slot; tile < total; tile += nb) {
+        const TileInfo ti = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
+        // per-lane DMA sources for this wave's ops (op q of this wave = rows
+        // [16*(q*NW + wave), +16) of the stage; rows < BM are A, the rest B)
+        const char* src[C::IPW];
+#pragma unroll
+        for (int q = 0; q < C::IPW; ++q) {
+            const int op = q * C::NW + wave;
+            const int row = op * 16 + lrow;
+            const char* p = a.w;  // dummy for ops past the end (never issued)
+            if (op < C::NINS) {
+                if (row < C::BM) {
+                    const int rr = ti.m0 + row;
+                    long r = 0;
+                    if (rr < ti.nrows) {
+                        if (MODE == FC1) {
+                            const int tok = (ti.g < a.E) ? a.permuted_pair[ti.row0 + rr] / a.k : rr;
+                            r = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+                        } else {
+                            r = ti.row0 + rr;
+                        }
+                    } else {
+                        r = (MODE == FC1) ? 0 : ti.row0;  // padding rows: any valid row
+                    }
+                    p = a.a_src + (size_t)r * a_ld;
+                } else {
+                    const int j = row - C::BM;
+                    int wrow;
+                    if (MODE == FC1) {
+                        const int blk = j >> 4, pair = blk >> 1;
+                        const int col = ti.nt * (C::BN / 2) + pair * 16 + (j & 15);
+                        wrow = (blk & 1) ? a.I + col : col;
+                    } else {
+                        wrow = min(ti.nt * C::BN + j, a.N - 1);
+                    }
+                    p = a.w + ((size_t)ti.g * a.N + wrow) * w_ld;
+                }
+            }
+            src[q] = p + lchunk * 16;
+        }
+        const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds;
+        auto issue = [&](int st, int kt) {
+#pragma unroll
+            for (int q = 0; q < C::IPW; ++q) {
+                const int op = q * C::NW + wave;
+                if (op < C::NINS)
+                    dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + op * 1024),
+                          src[q] + (size_t)kt * 64);
+            }
+        };
+
+        f32x4_t acc[C::MI][C::NI];
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int s = 0; s < C::S - 1; ++s)
+            if (s < nk) issue(s, s);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            // this wave's loads of stage kt are complete once at most the
+            // (already issued) later stages remain outstanding
+            const int later = min(C::S - 2, nk - 1 - kt);
+            if (later >= 2) wait_vmcnt<2 * C::IPW_MIN>();
+            else if (later == 1) wait_vmcnt<C::IPW_MIN>();
+            else wait_vmcnt<0>();
+            lds_barrier();  // every wave's part of stage kt is in LDS; slot (kt-1)%S is free
+            if (kt + C::S - 1 < nk) issue((kt + C::S - 1) % C::S, kt + C::S - 1);
+
+            const char* la = lds + (kt % C::S) * C::STAGE;
+            const char* lb = la + C::BM * C::ROWB;
+            u32x4_t fa[C::MI], fb[C::NI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+                fa[mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off(wm * C::WTM + mi * 16 + (lane & 15), lane >> 4));
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                fb[ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off(wn * C::WTN + ni * 16 + (lane & 15), lane >> 4));
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+        }
+        __syncthreads();  // all reads of the ring done before the next tile's prologue writes it
+
+        bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
+        if (MODE == FC1) {
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int q = 0; q < C::NI / 2; ++q) {
+                    const int pair = (wn * C::WTN) / 32 + q;
+                    const int col = ti.nt * (C::BN / 2) + pair * 16 + (lane & 15);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = ti.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < ti.nrows) {
+                            const float gt = acc[mi][2 * q][i];
+                            const float up = acc[mi][2 * q + 1][i];
+                            const float hv = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
+                            store_out(out + (size_t)(ti.row0 + rr) * a.out_ld + col, hv);
+                        }
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    const int col = ti.nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = ti.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < ti.nrows && col < a.N)
+                            store_out(out + (size_t)(ti.row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
+                    }
+                }
+        }
+        // stores count in vmcnt too: drain them so the next tile's stage waits
+        // count only its own DMA transfers
+        wait_vmcnt<0>();
+    }
+}
+
+template <int MODE, class C>
+moe_status run_dma_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s, int kid)
+{
+    auto kern = dma_gemm_kernel<MODE, C>;
+    static int occ = -1;
+    if (occ < 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, 0) != hipSuccess || n < 1) n = 1;
+        occ = n;
+    }
+    args.lo_rows = lo_rows;
+    args.hi_rows = hi_rows;
+    const long max_tiles = (long)(R / C::BM + args.G) * ((args.N + C::BN - 1) / C::BN);
+    long grid = (long)device_cu_count() * occ;
+    if (grid > max_tiles) grid = max_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    {
+        TimedLaunch tl(kid, s);
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, args);
+    }
+    return launch_status(MODE == FC1 ? "fc1 dma_gemm_kernel" : "fc2 dma_gemm_kernel");
+}
+
 template <class AT, class WT, int MODE, class C>
-moe_status run_gemm(const FfnArgs& args, int rows_upper, int ntiles_n, hipStream_t s, int kid)
+moe_status run_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s, int kid)
 {
     auto kern = grouped_gemm_kernel<AT, WT, MODE, C>;
     static int occ = -1;
@@ -388,7 +703,9 @@ moe_status run_gemm(const FfnArgs& args, int rows_upper, int ntiles_n, hipStream
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, 0) != hipSuccess || n < 1) n = 1;
         occ = n;
     }
-    const long max_tiles = (long)((rows_upper + C::BM - 1) / C::BM + args.G) * ntiles_n;
+    args.lo_rows = lo_rows;
+    args.hi_rows = hi_rows;
+    const long max_tiles = (long)(R / C::BM + args.G) * ((args.N + C::BN - 1) / C::BN);
     long grid = (long)device_cu_count() * occ;
     if (grid > max_tiles) grid = max_tiles;
     if (grid >= 8) grid -= grid % 8;
@@ -400,24 +717,67 @@ moe_status run_gemm(const FfnArgs& args, int rows_upper, int ntiles_n, hipStream
     return launch_status(MODE == FC1 ? "fc1 grouped_gemm_kernel" : "fc2 grouped_gemm_kernel");
 }
 
-template <class AT, class WT>
-moe_status run_ffn(const FfnArgs& fc1, const FfnArgs& fc2, int R, int G, hipStream_t s)
+// Row classes: each group goes to the tile shape that suits its row count.
+//   [0, 64)     32x128 tiles, 4 waves: weight streaming for decode-like groups
+//   [64, 384)   128x256 tiles, 8 waves
+//   [384, inf)  256x256 tiles, 8 waves: MFMA-bound groups
+constexpr int kMidRows = 64;
+constexpr int kBigRows = 384;
+constexpr int kAllRows = 1 << 30;
+
+template <class AT, class WT, int MODE>
+moe_status run_classes(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-    // Tile shape from the mean rows per group: skinny groups (decode-like)
-    // stream weights with a 32-row tile; larger groups use 128x128.
-    const bool skinny = R <= 48 * G;
-    moe_status st;
-    if (skinny) {
-        using C = Cfg<AT, WT, 32, 128, 1, 4>;
-        st = run_gemm<AT, WT, FC1, C>(fc1, R, fc1.N / C::BN, s, MOE_KID_FC1);
-        if (st != MOE_OK) return st;
-        return run_gemm<AT, WT, FC2, C>(fc2, R, fc2.N / C::BN, s, MOE_KID_FC2);
-    } else {
-        using C = Cfg<AT, WT, 128, 128, 2, 2>;
-        st = run_gemm<AT, WT, FC1, C>(fc1, R, fc1.N / C::BN, s, MOE_KID_FC1);
-        if (st != MOE_OK) return st;
-        return run_gemm<AT, WT, FC2, C>(fc2, R, fc2.N / C::BN, s, MOE_KID_FC2);
-    }
+    using Skinny = Cfg<AT, WT, 32, 128, 1, 4, 1>;
+    using Mid = Cfg<AT, WT, 128, 256, 2, 4, 2>;
+    // fp8 weights keep a second (per-scale-block) accumulator set, which does not
+    // fit a 256x256 tile's registers: they use the 128x256 shape for big groups
+    using Big = typename std::conditional<sizeof(WT) == 1, Mid, Cfg<AT, WT, 256, 256, 2, 4, 4>>::type;
+    moe_status st = run_gemm<AT, WT, MODE, Skinny>(f, 0, kMidRows, R, s, kid);
+    if (st != MOE_OK) return st;
+    st = run_gemm<AT, WT, MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
+    if (st != MOE_OK) return st;
+    return run_gemm<AT, WT, MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
+}
+
+// bf16 activations and weights: mid and big groups on the direct-to-LDS engine.
+template <int MODE>
+moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
+{
+    using Skinny = Cfg<bf16_t, bf16_t, 32, 128, 1, 4, 1>;
+    using Mid = DmaCfg<128, 256, 2, 4, 2, 4>;
+    using Big = DmaCfg<256, 256, 2, 4, 4, 4>;
+    moe_status st = run_gemm<bf16_t, bf16_t, MODE, Skinny>(f, 0, kMidRows, R, s, kid);
+    if (st != MOE_OK) return st;
+    st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
+    if (st != MOE_OK) return st;
+    return run_dma_gemm<MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
+}
+
+template <class AT, class WT>
+moe_status run_ffn(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
+{
+    moe_status st = run_classes<AT, WT, FC1>(fc1, R, s, MOE_KID_FC1);
+    if (st != MOE_OK) return st;
+    return run_classes<AT, WT, FC2>(fc2, R, s, MOE_KID_FC2);
+}
+
+template <>
+moe_status run_ffn<bf16_t, bf16_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
+{
+    moe_status st = run_classes_bf16<FC1>(fc1, R, s, MOE_KID_FC1);
+    if (st != MOE_OK) return st;
+    return run_classes_bf16<FC2>(fc2, R, s, MOE_KID_FC2);
+}
+
+// fp32 (small reference-precision layers): one 32x128 tile shape for all groups.
+template <>
+moe_status run_ffn<float, float>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
+{
+    using C = Cfg<float, float, 32, 128, 1, 4, 1>;
+    moe_status st = run_gemm<float, float, FC1, C>(fc1, 0, kAllRows, R, s, MOE_KID_FC1);
+    if (st != MOE_OK) return st;
+    return run_gemm<float, float, FC2, C>(fc2, 0, kAllRows, R, s, MOE_KID_FC2);
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -452,9 +812,9 @@ moe_status launch_ffn(const void* x, int act, int T, int H, int I, int k, int E,
     f2.wscale = w2_scale;
     f2.out = static_cast<char*>(fc2_out);
     f2.N = H; f2.K = I; f2.out_ld = H;
-    if (act == MOE_F32) return run_ffn<float, float>(f1, f2, R, G, s);
-    if (wdt == MOE_FP8_E4M3) return run_ffn<bf16_t, fp8_t>(f1, f2, R, G, s);
-    return run_ffn<bf16_t, bf16_t>(f1, f2, R, G, s);
+    if (act == MOE_F32) return run_ffn<float, float>(f1, f2, R, s);
+    if (wdt == MOE_FP8_E4M3) return run_ffn<bf16_t, fp8_t>(f1, f2, R, s);
+    return run_ffn<bf16_t, bf16_t>(f1, f2, R, s);
 }
 
 }  // namespace moe
