@@ -445,24 +445,43 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 // anything in VGPRs; one barrier per slice.  Chunk c of row r is stored at
 // chunk c ^ ((r >> 1) & 3) (measured conflict-free on gfx950 for both the
 // 16-row x 4-chunk fragment reads and the DMA writes).
-template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool PIPE_ = true, int ROWB_ = 64>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
+    // PIPE: fragments double-buffered in registers with the barrier between the
+    // two halves of a slice's MFMAs (for blocks with 2 waves per SIMD); without
+    // it, each slice reads its fragments after the barrier (more waves per SIMD
+    // hide that latency instead of registers)
+    static constexpr bool PIPE = PIPE_;
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
-    static constexpr int BK = 32;                          // K per stage
-    static constexpr int ROWB = 64;                        // bytes per staged row
+    static constexpr int ROWB = ROWB_;                     // bytes per staged row (64 or 128)
+    static constexpr int BK = ROWB / 2;                    // K per stage (bf16)
+    static constexpr int KSTEPS = BK / 32;                 // MFMA K-steps per stage
+    static constexpr int RPO = 1024 / ROWB;                // rows per 1 KB DMA op
     static constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
-    static constexpr int NINS = (BM + BN) / 16;            // 1 KB DMA ops per stage
+    static constexpr int NINS = (BM + BN) / RPO;           // 1 KB DMA ops per stage
     static constexpr int IPW = (NINS + NW - 1) / NW;       // max per wave
     static constexpr int IPW_MIN = NINS / NW;              // min per wave
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
     static_assert(BM % 16 == 0 && BN % 16 == 0 && WTM % 16 == 0 && WTN % 32 == 0, "tile");
     static_assert(IPW_MIN >= 1, "every wave issues loads");
+    static_assert(!PIPE || MI % 2 == 0, "the MFMA rows are issued in two halves");
+    static_assert(!PIPE || ROWB == 64, "the pipelined slice loop takes one K-step per slice");
+    static_assert(S >= 2 && (ROWB == 64 || ROWB == 128), "ring");
 };
 
-__device__ __forceinline__ int dma_off(int row, int kc) { return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4); }
+// Byte offset of logical 16-byte chunk kc of staged row `row`.  64-byte rows:
+// chunk kc ^ ((row >> 1) & 3); 128-byte rows: chunk kc ^ (row & 7).  Both were
+// measured free of bank conflicts on gfx950 for the fragment reads (16 rows x
+// 4 chunks per ds_read_b128) and for the 1 KB DMA writes.
+template <int ROWB>
+__device__ __forceinline__ int dma_off(int row, int kc)
+{
+    if (ROWB == 64) return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4);
+    return row * 128 + ((kc ^ (row & 7)) << 4);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -539,9 +558,11 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     const int nk = a.K / C::BK;
     const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * 2;
 
-    // this lane's row within a DMA op and the logical chunk it fetches
-    const int lrow = lane >> 2;
-    const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    // this lane's row within a DMA op and the logical chunk it fetches (the op
+    // writes lane l's 16 bytes at byte 16*l: row l / (ROWB/16), physical chunk
+    // l % (ROWB/16), which holds logical chunk physical ^ swizzle(row))
+    const int lrow = (C::ROWB == 64) ? (lane >> 2) : (lane >> 3);
+    const int lchunk = (C::ROWB == 64) ? ((lane & 3) ^ ((lane >> 3) & 3)) : ((lane & 7) ^ (lane >> 3));
 
     for (int tile = slot; tile < total; tile += nb) {
         const TileInfo ti = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
@@ -551,7 +572,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 #pragma unroll
         for (int q = 0; q < C::IPW; ++q) {
             const int op = q * C::NW + wave;
-            const int row = op * 16 + lrow;
+            const int row = op * C::RPO + lrow;
             const char* p = a.w;  // dummy for ops past the end (never issued)
             if (op < C::NINS) {
                 if (row < C::BM) {
@@ -590,7 +611,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 const int op = q * C::NW + wave;
                 if (op < C::NINS)
                     dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + op * 1024),
-                          src[q] + (size_t)kt * 64);
+                          src[q] + (size_t)kt * C::ROWB);
             }
         };
 
@@ -600,33 +621,83 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-        for (int s = 0; s < C::S - 1; ++s)
-            if (s < nk) issue(s, s);
-
-        for (int kt = 0; kt < nk; ++kt) {
-            // this wave's loads of stage kt are complete once at most the
-            // (already issued) later stages remain outstanding
-            const int later = min(C::S - 2, nk - 1 - kt);
-            if (later >= 2) wait_vmcnt<2 * C::IPW_MIN>();
-            else if (later == 1) wait_vmcnt<C::IPW_MIN>();
-            else wait_vmcnt<0>();
-            lds_barrier();  // every wave's part of stage kt is in LDS; slot (kt-1)%S is free
-            if (kt + C::S - 1 < nk) issue((kt + C::S - 1) % C::S, kt + C::S - 1);
-
-            const char* la = lds + (kt % C::S) * C::STAGE;
+        // Software pipeline.  Fragments of slice kt sit in register set kt&1;
+        // slice kt's MFMAs are split in two halves, and between them the wave
+        // waits for slice kt+1's DMA, joins the barrier that publishes it,
+        // refills the ring slot slice kt came from (its fragments are already
+        // in registers everywhere) with slice kt+S, and reads slice kt+1's
+        // fragments, whose latency the second half of the MFMAs covers.
+        u32x4_t fa[2][C::MI], fb[2][C::NI];
+        auto read_frags = [&](int set, int st, int ks) {
+            const char* la = lds + st * C::STAGE;
             const char* lb = la + C::BM * C::ROWB;
-            u32x4_t fa[C::MI], fb[C::NI];
+            const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
-                fa[mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off(wm * C::WTM + mi * 16 + (lane & 15), lane >> 4));
+                fa[set][mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off<C::ROWB>(wm * C::WTM + mi * 16 + (lane & 15), kc));
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                fb[ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off(wn * C::WTN + ni * 16 + (lane & 15), lane >> 4));
+                fb[set][ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off<C::ROWB>(wn * C::WTN + ni * 16 + (lane & 15), kc));
+        };
+        auto mfma_rows = [&](int set, int m_lo, int m_hi) {
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
+                if (mi >= m_lo && mi < m_hi)
 #pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+                    for (int ni = 0; ni < C::NI; ++ni)
+                        acc[mi][ni] = mfma_frag(fa[set][mi], fb[set][ni], acc[mi][ni], bf16_t());
+        };
+        // wait until this wave's DMA for the slice `later` stages before the
+        // newest issued one has landed
+        auto wait_stage = [&](int later) {
+            if (later >= 3) wait_vmcnt<3 * C::IPW_MIN>();
+            else if (later == 2) wait_vmcnt<2 * C::IPW_MIN>();
+            else if (later == 1) wait_vmcnt<C::IPW_MIN>();
+            else wait_vmcnt<0>();
+        };
+
+        if (!C::PIPE) {
+            // prologue: S-1 slices in flight; slot (kt-1)%S is refilled after
+            // the barrier that follows its last reads
+#pragma unroll
+            for (int st = 0; st < C::S - 1; ++st)
+                if (st < nk) issue(st, st);
+            for (int kt = 0; kt < nk; ++kt) {
+                wait_stage(min(C::S - 2, nk - 1 - kt));
+                lds_barrier();
+                if (kt + C::S - 1 < nk) issue((kt + C::S - 1) % C::S, kt + C::S - 1);
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                    read_frags(ks & 1, kt % C::S, ks);
+                    mfma_rows(ks & 1, 0, C::MI);
+                }
+            }
+        } else {
+#pragma unroll
+        for (int st = 0; st < C::S; ++st)
+            if (st < nk) issue(st, st);
+        wait_stage(min(C::S - 1, nk - 1));
+        lds_barrier();
+        read_frags(0, 0, 0);
+
+        for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kt + half;  // slice computed now, from set `half`
+                if (k < nk) {
+                    mfma_rows(half, 0, C::MI / 2);
+                    if (k + 1 < nk) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_stage(min(C::S - 2, nk - 2 - k));
+                        lds_barrier();
+                        if (k + C::S < nk) issue(k % C::S, k + C::S);
+                        read_frags(half ^ 1, (k + 1) % C::S, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    mfma_rows(half, C::MI / 2, C::MI);
+                }
+            }
+        }
         }
         __syncthreads();  // all reads of the ring done before the next tile's prologue writes it
 
@@ -746,7 +817,12 @@ moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
     using Skinny = Cfg<bf16_t, bf16_t, 32, 128, 1, 4, 1>;
     using Mid = DmaCfg<128, 256, 2, 4, 2, 4>;
-    using Big = DmaCfg<256, 256, 2, 4, 4, 4>;
+#ifndef MOE_BIG_CFG
+#define MOE_BIG_CFG 2
+#endif
+    using Big = typename std::conditional<MOE_BIG_CFG == 0, DmaCfg<256, 256, 2, 4, 4, 4>,
+                typename std::conditional<MOE_BIG_CFG == 1, DmaCfg<256, 256, 4, 4, 4, 4, false>,
+                                          DmaCfg<256, 256, 4, 4, 4, 2, false, 128>>::type>::type;
     moe_status st = run_gemm<bf16_t, bf16_t, MODE, Skinny>(f, 0, kMidRows, R, s, kid);
     if (st != MOE_OK) return st;
     st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
