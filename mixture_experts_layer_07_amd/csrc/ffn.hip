@@ -815,15 +815,22 @@ moe_status run_classes(const FfnArgs& f, int R, hipStream_t s, int kid)
 template <int MODE>
 moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
+#ifndef MOE_SMALL_CFG
+#define MOE_SMALL_CFG 1
+#endif
     using Skinny = Cfg<bf16_t, bf16_t, 32, 128, 1, 4, 1>;
-    using Mid = DmaCfg<128, 256, 2, 4, 2, 4>;
+    using SkinnyDma = DmaCfg<32, 256, 1, 4, 2, 4, false, 128>;
+    using Mid = typename std::conditional<MOE_SMALL_CFG == 0, DmaCfg<128, 256, 2, 4, 2, 4>,
+                                          DmaCfg<128, 256, 4, 4, 2, 3, false, 128>>::type;
 #ifndef MOE_BIG_CFG
 #define MOE_BIG_CFG 2
 #endif
     using Big = typename std::conditional<MOE_BIG_CFG == 0, DmaCfg<256, 256, 2, 4, 4, 4>,
                 typename std::conditional<MOE_BIG_CFG == 1, DmaCfg<256, 256, 4, 4, 4, 4, false>,
-                                          DmaCfg<256, 256, 4, 4, 4, 2, false, 128>>::type>::type;
-    moe_status st = run_gemm<bf16_t, bf16_t, MODE, Skinny>(f, 0, kMidRows, R, s, kid);
+                typename std::conditional<MOE_BIG_CFG == 3, DmaCfg<256, 256, 2, 4, 4, 2, false, 128>,
+                                          DmaCfg<256, 256, 4, 4, 4, 2, false, 128>>::type>::type>::type;
+    moe_status st = (MOE_SMALL_CFG == 0) ? run_gemm<bf16_t, bf16_t, MODE, Skinny>(f, 0, kMidRows, R, s, kid)
+                                          : run_dma_gemm<MODE, SkinnyDma>(f, 0, kMidRows, R, s, kid);
     if (st != MOE_OK) return st;
     st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
     if (st != MOE_OK) return st;
