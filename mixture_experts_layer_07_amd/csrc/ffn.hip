@@ -438,21 +438,18 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 // ---------------------------------------------------------------------------
 // bf16 x bf16 tile engine with direct global->LDS loads.
 //
-// Each stage is a 64-byte K slice (32 bf16) of BM activation rows and BN weight
-// rows, written straight into LDS by global_load_lds_dwordx4: one instruction
-// moves 1 KB = 16 rows x 64 B, lane l landing at byte 16*l of it.  The ring
-// holds S stages, so loads run S-1 slices ahead of the MFMAs without holding
-// anything in VGPRs; one barrier per slice.  Chunk c of row r is stored at
-// chunk c ^ ((r >> 1) & 3) (measured conflict-free on gfx950 for both the
-// 16-row x 4-chunk fragment reads and the DMA writes).
-template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool PIPE_ = true, int ROWB_ = 64>
+// Each stage is one K slice of ROWB bytes (64 bf16 for 128-byte rows) of BM
+// activation rows and BN weight rows, written straight into LDS by
+// global_load_lds_dwordx4: one instruction moves 1 KB, lane l landing at byte
+// 16*l, i.e. 1024/ROWB whole rows, so every lane request is a full 128-byte
+// line for 128-byte rows.  A ring of S stages keeps S-1 slices in flight
+// without holding anything in VGPRs; one LDS-only barrier per slice.  The
+// next tile's token indices are fetched when a tile starts and its first
+// slices are issued before the current tile's epilogue, so a tile change
+// exposes only the epilogue's store drain.
+template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, int ROWB_ = 128>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
-    // PIPE: fragments double-buffered in registers with the barrier between the
-    // two halves of a slice's MFMAs (for blocks with 2 waves per SIMD); without
-    // it, each slice reads its fragments after the barrier (more waves per SIMD
-    // hide that latency instead of registers)
-    static constexpr bool PIPE = PIPE_;
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
     static constexpr int ROWB = ROWB_;                     // bytes per staged row (64 or 128)
@@ -461,15 +458,12 @@ struct DmaCfg {
     static constexpr int RPO = 1024 / ROWB;                // rows per 1 KB DMA op
     static constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
     static constexpr int NINS = (BM + BN) / RPO;           // 1 KB DMA ops per stage
-    static constexpr int IPW = (NINS + NW - 1) / NW;       // max per wave
-    static constexpr int IPW_MIN = NINS / NW;              // min per wave
+    static constexpr int IPW = NINS / NW;                  // ops per wave per stage
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static_assert(BM % 16 == 0 && BN % 16 == 0 && WTM % 16 == 0 && WTN % 32 == 0, "tile");
-    static_assert(IPW_MIN >= 1, "every wave issues loads");
-    static_assert(!PIPE || MI % 2 == 0, "the MFMA rows are issued in two halves");
-    static_assert(!PIPE || ROWB == 64, "the pipelined slice loop takes one K-step per slice");
-    static_assert(S >= 2 && (ROWB == 64 || ROWB == 128), "ring");
+    static_assert(BM % RPO == 0 && NINS % NW == 0 && IPW >= 1, "DMA ops split evenly over waves");
+    static_assert(WTM % 16 == 0 && WTN % 32 == 0, "tile");
+    static_assert(S >= 2 && S <= 4 && (ROWB == 64 || ROWB == 128), "ring");
 };
 
 // Byte offset of logical 16-byte chunk kc of staged row `row`.  64-byte rows:
@@ -526,6 +520,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     const int G = a.G;
     const int ntiles_n = (a.N + C::BN - 1) / C::BN;
 
+    // ---- flattened tile list of this launch's row class (as in grouped_gemm_kernel)
     for (int g = tid; g <= G; g += C::NT) s_off[g] = a.offsets[g];
     __syncthreads();
     if (wave == 0) {
@@ -555,65 +550,95 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     const int nb = gridDim.x;
     const bool xcd_map = (nb % 8) == 0;
     const int slot = xcd_map ? (blockIdx.x >> 3) + (blockIdx.x & 7) * (nb >> 3) : blockIdx.x;
+    int tile = slot;
+    if (tile >= total) return;
+
     const int nk = a.K / C::BK;
     const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * 2;
-
+    const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds;
     // this lane's row within a DMA op and the logical chunk it fetches (the op
     // writes lane l's 16 bytes at byte 16*l: row l / (ROWB/16), physical chunk
     // l % (ROWB/16), which holds logical chunk physical ^ swizzle(row))
     const int lrow = (C::ROWB == 64) ? (lane >> 2) : (lane >> 3);
     const int lchunk = (C::ROWB == 64) ? ((lane & 3) ^ ((lane >> 3) & 3)) : ((lane & 7) ^ (lane >> 3));
 
-    for (int tile = slot; tile < total; tile += nb) {
-        const TileInfo ti = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
-        // per-lane DMA sources for this wave's ops (op q of this wave = rows
-        // [16*(q*NW + wave), +16) of the stage; rows < BM are A, the rest B)
-        const char* src[C::IPW];
-#pragma unroll
-        for (int q = 0; q < C::IPW; ++q) {
-            const int op = q * C::NW + wave;
-            const int row = op * C::RPO + lrow;
-            const char* p = a.w;  // dummy for ops past the end (never issued)
-            if (op < C::NINS) {
-                if (row < C::BM) {
-                    const int rr = ti.m0 + row;
-                    long r = 0;
-                    if (rr < ti.nrows) {
-                        if (MODE == FC1) {
-                            const int tok = (ti.g < a.E) ? a.permuted_pair[ti.row0 + rr] / a.k : rr;
-                            r = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
-                        } else {
-                            r = ti.row0 + rr;
-                        }
-                    } else {
-                        r = (MODE == FC1) ? 0 : ti.row0;  // padding rows: any valid row
-                    }
-                    p = a.a_src + (size_t)r * a_ld;
-                } else {
-                    const int j = row - C::BM;
-                    int wrow;
-                    if (MODE == FC1) {
-                        const int blk = j >> 4, pair = blk >> 1;
-                        const int col = ti.nt * (C::BN / 2) + pair * 16 + (j & 15);
-                        wrow = (blk & 1) ? a.I + col : col;
-                    } else {
-                        wrow = min(ti.nt * C::BN + j, a.N - 1);
-                    }
-                    p = a.w + ((size_t)ti.g * a.N + wrow) * w_ld;
-                }
+    // Source row of this lane for op q of tile ti: op q of this wave stages
+    // rows [RPO*(q*NW + wave), +RPO); rows < BM are A rows, the rest B rows.
+    // For FC1 A rows the token comes from permuted_pair: a_raw() only loads the
+    // entry (from an always-valid address) and source() interprets it, so the
+    // next tile's loads can be issued early and consumed a whole tile later.
+    auto a_raw = [&](const TileInfo& ti, int q) -> int {
+        const int row = (q * C::NW + wave) * C::RPO + lrow;
+        if (MODE == FC2 || row >= C::BM) return 0;
+        const int rr = ti.m0 + row;
+        const int i = (ti.g < a.E && rr < ti.nrows) ? ti.row0 + rr : 0;
+        // global-space load: a flat load would also count in lgkmcnt and make
+        // the LDS-only barriers wait for it
+        return *(const __attribute__((address_space(1))) int*)(a.permuted_pair + i);
+    };
+    auto source = [&](const TileInfo& ti, int q, int raw) -> const char* {
+        const int row = (q * C::NW + wave) * C::RPO + lrow;
+        const char* p;
+        if (row < C::BM) {
+            const int rr = ti.m0 + row;
+            long r;
+            if (MODE == FC1) {
+                int tok = (rr >= ti.nrows) ? 0 : (ti.g < a.E ? raw / a.k : rr);  // padding rows: token 0
+                r = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            } else {
+                r = ti.row0 + (rr < ti.nrows ? rr : 0);
             }
-            src[q] = p + lchunk * 16;
+            p = a.a_src + (size_t)r * a_ld;
+        } else {
+            const int j = row - C::BM;
+            int wrow;
+            if (MODE == FC1) {
+                const int blk = j >> 4, pair = blk >> 1;
+                const int col = ti.nt * (C::BN / 2) + pair * 16 + (j & 15);
+                wrow = (blk & 1) ? a.I + col : col;
+            } else {
+                wrow = min(ti.nt * C::BN + j, a.N - 1);  // partial last N-tile
+            }
+            p = a.w + ((size_t)ti.g * a.N + wrow) * w_ld;
         }
-        const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds;
-        auto issue = [&](int st, int kt) {
+        return p + lchunk * 16;
+    };
+    const char* src[C::IPW];
+    auto issue = [&](int st, int kt) {
 #pragma unroll
-            for (int q = 0; q < C::IPW; ++q) {
-                const int op = q * C::NW + wave;
-                if (op < C::NINS)
-                    dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + op * 1024),
-                          src[q] + (size_t)kt * C::ROWB);
-            }
-        };
+        for (int q = 0; q < C::IPW; ++q)
+            dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + (q * C::NW + wave) * 1024),
+                  src[q] + (size_t)kt * C::ROWB);
+    };
+    auto wait_stage = [&](int later) {  // this wave's slice with `later` newer slices in flight has landed
+        if (later >= 2) wait_vmcnt<2 * C::IPW>();
+        else if (later == 1) wait_vmcnt<C::IPW>();
+        else wait_vmcnt<0>();
+    };
+
+    TileInfo cur = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
+    {
+        int idx[C::IPW];
+#pragma unroll
+        for (int q = 0; q < C::IPW; ++q) idx[q] = a_raw(cur, q);
+#pragma unroll
+        for (int q = 0; q < C::IPW; ++q) src[q] = source(cur, q, idx[q]);
+    }
+    int ring = 0;  // ring slot of the current tile's slice 0
+#pragma unroll
+    for (int st = 0; st < C::S - 1; ++st)
+        if (st < nk) issue(st, st);
+
+    while (true) {
+        const int next_tile = tile + nb;
+        const bool has_next = next_tile < total;
+        TileInfo nxt = cur;
+        int nidx[C::IPW];
+        if (has_next) {
+            nxt = decode_tile<C>(next_tile, s_off, s_tile0, G, ntiles_n);
+#pragma unroll
+            for (int q = 0; q < C::IPW; ++q) nidx[q] = a_raw(nxt, q);
+        }
 
         f32x4_t acc[C::MI][C::NI];
 #pragma unroll
@@ -621,85 +646,39 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Software pipeline.  Fragments of slice kt sit in register set kt&1;
-        // slice kt's MFMAs are split in two halves, and between them the wave
-        // waits for slice kt+1's DMA, joins the barrier that publishes it,
-        // refills the ring slot slice kt came from (its fragments are already
-        // in registers everywhere) with slice kt+S, and reads slice kt+1's
-        // fragments, whose latency the second half of the MFMAs covers.
-        u32x4_t fa[2][C::MI], fb[2][C::NI];
-        auto read_frags = [&](int set, int st, int ks) {
-            const char* la = lds + st * C::STAGE;
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_stage(min(C::S - 2, nk - 1 - kt));
+            lds_barrier();  // slice kt is in LDS for every wave; slot of slice kt-1 is free
+            if (kt + C::S - 1 < nk) issue((ring + kt + C::S - 1) % C::S, kt + C::S - 1);
+            const char* la = lds + ((ring + kt) % C::S) * C::STAGE;
             const char* lb = la + C::BM * C::ROWB;
-            const int kc = ks * 4 + (lane >> 4);
 #pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-                fa[set][mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off<C::ROWB>(wm * C::WTM + mi * 16 + (lane & 15), kc));
+            for (int ks = 0; ks < C::KSTEPS; ++ks) {
+                const int kc = ks * 4 + (lane >> 4);
+                u32x4_t fa[C::MI], fb[C::NI];
 #pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                fb[set][ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off<C::ROWB>(wn * C::WTN + ni * 16 + (lane & 15), kc));
-        };
-        auto mfma_rows = [&](int set, int m_lo, int m_hi) {
+                for (int mi = 0; mi < C::MI; ++mi)
+                    fa[mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off<C::ROWB>(wm * C::WTM + mi * 16 + (lane & 15), kc));
 #pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-                if (mi >= m_lo && mi < m_hi)
+                for (int ni = 0; ni < C::NI; ++ni)
+                    fb[ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off<C::ROWB>(wn * C::WTN + ni * 16 + (lane & 15), kc));
 #pragma unroll
-                    for (int ni = 0; ni < C::NI; ++ni)
-                        acc[mi][ni] = mfma_frag(fa[set][mi], fb[set][ni], acc[mi][ni], bf16_t());
-        };
-        // wait until this wave's DMA for the slice `later` stages before the
-        // newest issued one has landed
-        auto wait_stage = [&](int later) {
-            if (later >= 3) wait_vmcnt<3 * C::IPW_MIN>();
-            else if (later == 2) wait_vmcnt<2 * C::IPW_MIN>();
-            else if (later == 1) wait_vmcnt<C::IPW_MIN>();
-            else wait_vmcnt<0>();
-        };
+                for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+            }
+        }
 
-        if (!C::PIPE) {
-            // prologue: S-1 slices in flight; slot (kt-1)%S is refilled after
-            // the barrier that follows its last reads
+        // the next tile's first slices go out before this tile's epilogue
+        lds_barrier();  // every wave is done reading the ring
+        if (has_next) {
+#pragma unroll
+            for (int q = 0; q < C::IPW; ++q) src[q] = source(nxt, q, nidx[q]);
+            ring = (ring + nk) % C::S;
 #pragma unroll
             for (int st = 0; st < C::S - 1; ++st)
-                if (st < nk) issue(st, st);
-            for (int kt = 0; kt < nk; ++kt) {
-                wait_stage(min(C::S - 2, nk - 1 - kt));
-                lds_barrier();
-                if (kt + C::S - 1 < nk) issue((kt + C::S - 1) % C::S, kt + C::S - 1);
-#pragma unroll
-                for (int ks = 0; ks < C::KSTEPS; ++ks) {
-                    read_frags(ks & 1, kt % C::S, ks);
-                    mfma_rows(ks & 1, 0, C::MI);
-                }
-            }
-        } else {
-#pragma unroll
-        for (int st = 0; st < C::S; ++st)
-            if (st < nk) issue(st, st);
-        wait_stage(min(C::S - 1, nk - 1));
-        lds_barrier();
-        read_frags(0, 0, 0);
-
-        for (int kt = 0; kt < nk; kt += 2) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int k = kt + half;  // slice computed now, from set `half`
-                if (k < nk) {
-                    mfma_rows(half, 0, C::MI / 2);
-                    if (k + 1 < nk) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        wait_stage(min(C::S - 2, nk - 2 - k));
-                        lds_barrier();
-                        if (k + C::S < nk) issue(k % C::S, k + C::S);
-                        read_frags(half ^ 1, (k + 1) % C::S, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    mfma_rows(half, C::MI / 2, C::MI);
-                }
-            }
+                if (st < nk) issue((ring + st) % C::S, st);
         }
-        }
-        __syncthreads();  // all reads of the ring done before the next tile's prologue writes it
 
         bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
         if (MODE == FC1) {
@@ -708,15 +687,15 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 #pragma unroll
                 for (int q = 0; q < C::NI / 2; ++q) {
                     const int pair = (wn * C::WTN) / 32 + q;
-                    const int col = ti.nt * (C::BN / 2) + pair * 16 + (lane & 15);
+                    const int col = cur.nt * (C::BN / 2) + pair * 16 + (lane & 15);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = ti.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < ti.nrows) {
+                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < cur.nrows) {
                             const float gt = acc[mi][2 * q][i];
                             const float up = acc[mi][2 * q + 1][i];
                             const float hv = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
-                            store_out(out + (size_t)(ti.row0 + rr) * a.out_ld + col, hv);
+                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, hv);
                         }
                     }
                 }
@@ -725,18 +704,21 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
-                    const int col = ti.nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
+                    const int col = cur.nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = ti.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < ti.nrows && col < a.N)
-                            store_out(out + (size_t)(ti.row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
+                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
+                        if (rr < cur.nrows && col < a.N)
+                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
                     }
                 }
         }
-        // stores count in vmcnt too: drain them so the next tile's stage waits
-        // count only its own DMA transfers
+        // drain: stores and the next tile's first slices; afterwards the stage
+        // waits count this block's DMA transfers only
         wait_vmcnt<0>();
+        if (!has_next) break;
+        tile = next_tile;
+        cur = nxt;
     }
 }
 
@@ -815,22 +797,13 @@ moe_status run_classes(const FfnArgs& f, int R, hipStream_t s, int kid)
 template <int MODE>
 moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-#ifndef MOE_SMALL_CFG
-#define MOE_SMALL_CFG 1
-#endif
-    using Skinny = Cfg<bf16_t, bf16_t, 32, 128, 1, 4, 1>;
-    using SkinnyDma = DmaCfg<32, 256, 1, 4, 2, 4, false, 128>;
-    using Mid = typename std::conditional<MOE_SMALL_CFG == 0, DmaCfg<128, 256, 2, 4, 2, 4>,
-                                          DmaCfg<128, 256, 4, 4, 2, 3, false, 128>>::type;
-#ifndef MOE_BIG_CFG
-#define MOE_BIG_CFG 2
-#endif
-    using Big = typename std::conditional<MOE_BIG_CFG == 0, DmaCfg<256, 256, 2, 4, 4, 4>,
-                typename std::conditional<MOE_BIG_CFG == 1, DmaCfg<256, 256, 4, 4, 4, 4, false>,
-                typename std::conditional<MOE_BIG_CFG == 3, DmaCfg<256, 256, 2, 4, 4, 2, false, 128>,
-                                          DmaCfg<256, 256, 4, 4, 4, 2, false, 128>>::type>::type>::type;
-    moe_status st = (MOE_SMALL_CFG == 0) ? run_gemm<bf16_t, bf16_t, MODE, Skinny>(f, 0, kMidRows, R, s, kid)
-                                          : run_dma_gemm<MODE, SkinnyDma>(f, 0, kMidRows, R, s, kid);
+    // shapes chosen by measurement on MI355X: 4 waves per SIMD for the large
+    // tiles (one wave alone cannot keep the MFMA pipe busy), 128-byte K slices
+    // (whole-line requests), a deeper ring for the weight-streaming skinny tiles
+    using Skinny = DmaCfg<32, 256, 1, 4, 2, 4>;
+    using Mid = DmaCfg<128, 256, 4, 4, 2, 3>;
+    using Big = DmaCfg<256, 256, 4, 4, 4, 2>;
+    moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid);
     if (st != MOE_OK) return st;
     st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
     if (st != MOE_OK) return st;
