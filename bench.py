@@ -95,6 +95,56 @@ def load_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def calibration_copy(mib, device):
+    """A plain streaming kernel of known traffic (reads and writes `mib` MiB once),
+    run before the workload so rocprofv3 FETCH_SIZE / WRITE_SIZE can be scaled."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
+    """Write profiles/fc1_<workload>_traffic.json from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy-mib N --no-decode --no-cpu-baseline` (FETCH_SIZE,
+    then WRITE_SIZE; counter values are KiB per dispatch).  FC1's HBM bytes per
+    step are the counters summed over its row-class launches, divided by the
+    number of layer calls, each scaled by true/counted bytes of the copy."""
+    import csv
+
+    def load(d, counter):
+        path = os.path.join(d, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            for root, _, files in os.walk(d):
+                for f in files:
+                    if f.endswith("counter_collection.csv"):
+                        path = os.path.join(root, f)
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        calib = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
+        fc1 = [float(r["Counter_Value"]) for r in rows
+               if ("dma_gemm_kernel<0," in r["Kernel_Name"]
+                   or ("grouped_gemm_kernel<" in r["Kernel_Name"] and ", 0, moe::" in r["Kernel_Name"]))]
+        calls = sum(1 for r in rows if "route_kernel" in r["Kernel_Name"])
+        if not calib or not fc1 or not calls:
+            raise SystemExit(f"{path}: calibration copy, FC1 or route dispatches missing")
+        scale = (copy_mib * 1024.0) / max(calib)
+        return sum(fc1) * 1024.0 * scale / calls, scale, calls
+    fetch, sf, n1 = load(fetch_dir, "FETCH_SIZE")
+    write, sw, n2 = load(write_dir, "WRITE_SIZE")
+    out = {"workload": workload, "kernel": "grouped GEMM FC1 (all row-class launches of a step)",
+           "kernel_source_sha": kernel_sha(), "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
+           "copy_calibration": {"mib": copy_mib, "fetch_scale": sf, "write_scale": sw},
+           "layer_calls_seen": [n1, n2], "commands": commands}
+    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def run_workload(name, steps, warmup, device):
     import torch
     import mixture_experts_layer_07_amd as moe
@@ -181,7 +231,17 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs into profiles/ and exit")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="command lines recorded in the traffic summary")
     args = ap.parse_args()
+    if args.traffic_from:
+        summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.workload,
+                          args.calibrate_copy_mib, args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the layer keeps all experts on one device "
               f"and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -191,6 +251,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.calibrate_copy_mib:
+        calibration_copy(args.calibrate_copy_mib, dev)
     main_res = run_workload(args.workload, args.steps, args.warmup, dev)
     w = main_res["w"]
     traffic = load_traffic(args.workload)
