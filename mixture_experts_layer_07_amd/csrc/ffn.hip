@@ -120,6 +120,37 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// 4x4 transpose across the four lanes of a quad (lanes 4k .. 4k+3): on entry
+// quad lane t holds v[i] = M[i][t], on exit v[i] = M[t][i].  Two butterfly
+// stages over DPP quad permutations; a register moves in a stage when its
+// index and the lane differ in that stage's bit.
+__device__ __forceinline__ void quad_transpose(float (&v)[4])
+{
+    const int t = threadIdx.x & 3;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // from lane t^1: quad_perm [1,0,3,2]
+        x[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i ^ 1]), 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if ((i ^ t) & 1) v[i] = x[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // from lane t^2: quad_perm [2,3,0,1]
+        x[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i ^ 2]), 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if ((i ^ t) & 2) v[i] = x[i];
+}
+
+// Four consecutive bf16 outputs (8 bytes, 8-byte aligned)
+__device__ __forceinline__ void store4_bf16(bf16_t* p, const float (&v)[4])
+{
+    const unsigned lo = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
+    const unsigned hi = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    *(__attribute__((address_space(1))) u32x2_t*)(p) = u32x2_t{lo, hi};
+}
+
 
 // 16-byte load through the global address space.  The tile pointers live in
 // a by-value struct and loop-carried registers, where the compiler cannot infer
@@ -185,19 +216,20 @@ template <class C>
 __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_off, const int* s_tile0,
                                                 int G, int ntiles_n)
 {
+    // every value here is block-uniform; readfirstlane keeps them in SGPRs
     int lo = 0, hi = G - 1;
     while (lo < hi) {  // last g with s_tile0[g] <= tile
         const int mid = (lo + hi + 1) >> 1;
-        if (s_tile0[mid] <= tile) lo = mid; else hi = mid - 1;
+        if (__builtin_amdgcn_readfirstlane(s_tile0[mid]) <= tile) lo = mid; else hi = mid - 1;
     }
     TileInfo ti;
     ti.g = lo;
-    ti.row0 = s_off[lo];
-    ti.nrows = s_off[lo + 1] - ti.row0;
+    ti.row0 = __builtin_amdgcn_readfirstlane(s_off[lo]);
+    ti.nrows = __builtin_amdgcn_readfirstlane(s_off[lo + 1]) - ti.row0;
     const int mtiles = (ti.nrows + C::BM - 1) / C::BM;
     // group-M order: runs of GM M-tiles share one N-tile, so a contiguous slice
     // of the list reuses both operands (A across N-tiles, B across M-tiles)
-    const int local = tile - s_tile0[lo];
+    const int local = tile - __builtin_amdgcn_readfirstlane(s_tile0[lo]);
     const int band = local / (C::GM * ntiles_n);
     const int first_m = band * C::GM;
     const int gm = min(mtiles - first_m, C::GM);
@@ -515,7 +547,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave values stay in SGPRs
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int G = a.G;
     const int ntiles_n = (a.N + C::BN - 1) / C::BN;
@@ -680,37 +712,41 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 if (st < nk) issue((ring + st) % C::S, st);
         }
 
+        // Epilogue.  An MFMA block leaves lane l with rows 4*(l/16) + i (i < 4)
+        // of column l%16; a quad transpose gives each lane one row and four
+        // consecutive columns (4*((l%16)/4) + i), stored as one 8-byte write.
         bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
+        const int erow = (lane >> 4) * 4 + (lane & 3);  // row within a 16x16 block
+        const int ecol = lane & 12;                      // first of its 4 columns
         if (MODE == FC1) {
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                 for (int q = 0; q < C::NI / 2; ++q) {
-                    const int pair = (wn * C::WTN) / 32 + q;
-                    const int col = cur.nt * (C::BN / 2) + pair * 16 + (lane & 15);
+                    float hv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < cur.nrows) {
-                            const float gt = acc[mi][2 * q][i];
-                            const float up = acc[mi][2 * q + 1][i];
-                            const float hv = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
-                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, hv);
-                        }
+                        const float gt = acc[mi][2 * q][i];
+                        const float up = acc[mi][2 * q + 1][i];
+                        hv[i] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
                     }
+                    quad_transpose(hv);
+                    const int pair = (wn * C::WTN) / 32 + q;
+                    const int col = cur.nt * (C::BN / 2) + pair * 16 + ecol;
+                    const int rr = cur.m0 + wm * C::WTM + mi * 16 + erow;
+                    if (rr < cur.nrows) store4_bf16(out + (size_t)(cur.row0 + rr) * a.out_ld + col, hv);
                 }
         } else {
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
-                    const int col = cur.nt * C::BN + wn * C::WTN + ni * 16 + (lane & 15);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = cur.m0 + wm * C::WTM + mi * 16 + (lane >> 4) * 4 + i;
-                        if (rr < cur.nrows && col < a.N)
-                            store_out(out + (size_t)(cur.row0 + rr) * a.out_ld + col, acc[mi][ni][i]);
-                    }
+                    float v[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
+                    quad_transpose(v);
+                    // N is a multiple of 16: a 16-column block is wholly inside or outside
+                    const int col = cur.nt * C::BN + wn * C::WTN + ni * 16 + ecol;
+                    const int rr = cur.m0 + wm * C::WTM + mi * 16 + erow;
+                    if (rr < cur.nrows && col < a.N) store4_bf16(out + (size_t)(cur.row0 + rr) * a.out_ld + col, v);
                 }
         }
         // drain: stores and the next tile's first slices; afterwards the stage
