@@ -178,6 +178,30 @@ def test_expert_ffn_empty_groups_and_one_hot():
     assert err1 < 1e-5
 
 
+# group sizes on both sides of every tile-shape and row-class boundary
+# (32/128/256-row tiles; classes [0,64), [64,384), [384,inf))
+CLASS_EDGE_ROWS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 513]
+
+
+@pytest.mark.parametrize("act,wdt", [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "f32")])
+def test_expert_ffn_row_class_boundaries(act, wdt):
+    counts = CLASS_EDGE_ROWS
+    E = len(counts)
+    T = sum(counts)
+    w = small_workload(act, wdt, T=T, H=256, I=256, E=E, k=1, method=0)
+    inp = wl.make_inputs(w, 4)
+    # top-1 routing that gives expert e exactly counts[e] tokens, in shuffled token order
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(4).shuffle(owner)
+    logits = torch.full((T, E), -5.0)
+    logits[torch.arange(T), torch.from_numpy(owner)] = 5.0
+    inp["logits"] = logits
+    err, got, ref = run_ffn_check(w, inp)
+    tol = TOL[(act, wdt)]
+    row_err = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err < tol and row_err.max() < 3 * tol, (err, row_err.max())
+
+
 def test_finalize_parity():
     """Finalize fed the oracle's FFN rows (rounded to bf16 / fp32)."""
     rng = np.random.default_rng(5)
