@@ -363,6 +363,28 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
         }
 
         for (int kt = 0; kt < nk; ++kt) {
+            // fp8: the block scales used at the end of this iteration are loaded
+            // before the next slice's loads, so that waiting for them does not
+            // also wait for those (loads complete in issue order)
+            const bool block_end = C::FP8 && ((kt + 1) * C::BK) % 128 == 0;
+            float bscale[C::FP8 ? C::NI : 1];
+            if (block_end) {
+                const int kb = (kt * C::BK) / 128;
+                const int sk = a.K / 128;
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    const int j = wn * C::WTN + ni * 16;  // first staged B row of this block
+                    int wrow;
+                    if (MODE == FC1) {
+                        const int blk = j >> 4, pair = blk >> 1;
+                        const int col = cur.nt * (C::BN / 2) + pair * 16;
+                        wrow = (blk & 1) ? a.I + col : col;
+                    } else {
+                        wrow = min(cur.nt * C::BN + j, a.N - 1);
+                    }
+                    bscale[C::FP8 ? ni : 0] = a.wscale[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kb];
+                }
+            }
             // issue the next slice's loads: this tile's, or the next tile's first
             bool staged = true;
             if (kt + 1 < nk) {
@@ -398,22 +420,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
                             acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], CT());
                     }
             }
-            if (C::FP8 && ((kt + 1) * C::BK) % 128 == 0) {
+            if (block_end) {
                 // end of a 128-wide K block: acc += block scale * partial
-                const int kb = (kt * C::BK) / 128;
-                const int sk = a.K / 128;
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
-                    const int j = wn * C::WTN + ni * 16;  // first staged B row of this block
-                    int wrow;
-                    if (MODE == FC1) {
-                        const int blk = j >> 4, pair = blk >> 1;
-                        const int col = cur.nt * (C::BN / 2) + pair * 16;
-                        wrow = (blk & 1) ? a.I + col : col;
-                    } else {
-                        wrow = min(cur.nt * C::BN + j, a.N - 1);
-                    }
-                    const float s = a.wscale[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kb];
+                    const float s = bscale[C::FP8 ? ni : 0];
 #pragma unroll
                     for (int mi = 0; mi < C::MI; ++mi) {
                         acc[mi][ni] += s * part[C::FP8 ? mi : 0][C::FP8 ? ni : 0];
@@ -468,46 +479,71 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 x bf16 tile engine with direct global->LDS loads.
+// Tile engine with direct global->LDS loads (bf16 activations; bf16 or fp8
+// weights).
 //
-// Each stage is one K slice of ROWB bytes (64 bf16 for 128-byte rows) of BM
-// activation rows and BN weight rows, written straight into LDS by
-// global_load_lds_dwordx4: one instruction moves 1 KB, lane l landing at byte
-// 16*l, i.e. 1024/ROWB whole rows, so every lane request is a full 128-byte
-// line for 128-byte rows.  A ring of S stages keeps S-1 slices in flight
-// without holding anything in VGPRs; one LDS-only barrier per slice.  The
-// next tile's token indices are fetched when a tile starts and its first
-// slices are issued before the current tile's epilogue, so a tile change
+// Each stage is one K slice of 64 values: BM activation rows of 128 bytes and
+// BN weight rows of 128 bytes (bf16) or 64 bytes (fp8), written straight into
+// LDS by global_load_lds_dwordx4: one instruction moves 1 KB, lane l landing
+// at byte 16*l, i.e. 8 activation rows or 8 bf16 / 16 fp8 weight rows, every
+// lane request a full line or half line.  A ring of S stages keeps S-1 slices
+// in flight without holding anything in VGPRs; one LDS-only barrier per
+// slice.  The next tile's token indices are fetched when a tile starts and its
+// first slices are issued before the current tile's epilogue, so a tile change
 // exposes only the epilogue's store drain.
-template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, int ROWB_ = 128>
+//
+// fp8 weights (W8): a lane reads its 8 fp8 values of a fragment from LDS and
+// widens them to bf16 (exact: every e4m3 value is a bf16 value); the MFMA
+// sums of one 128-wide K block go into a partial tile that is added to the
+// accumulator times the block's fp32 scale (exact in the scale), so the only
+// rounding besides fp32 accumulation is the one of the output.
+template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool W8_ = false>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
+    static constexpr bool W8 = W8_;
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
-    static constexpr int ROWB = ROWB_;                     // bytes per staged row (64 or 128)
-    static constexpr int BK = ROWB / 2;                    // K per stage (bf16)
+    static constexpr int BK = 64;                          // K per stage
     static constexpr int KSTEPS = BK / 32;                 // MFMA K-steps per stage
-    static constexpr int RPO = 1024 / ROWB;                // rows per 1 KB DMA op
-    static constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
-    static constexpr int NINS = (BM + BN) / RPO;           // 1 KB DMA ops per stage
+    static constexpr int BROWB = W8 ? 64 : 128;            // weight bytes per staged row
+    static constexpr int A_OPS = BM / 8;                   // 1 KB DMA ops per stage, activations
+    static constexpr int B_OPS = BN * BROWB / 1024;        // ... and weights
+    static constexpr int A_BYTES = BM * 128;
+    static constexpr int STAGE = A_BYTES + BN * BROWB;     // bytes per stage
+    static constexpr int NINS = A_OPS + B_OPS;
     static constexpr int IPW = NINS / NW;                  // ops per wave per stage
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static_assert(BM % RPO == 0 && NINS % NW == 0 && IPW >= 1, "DMA ops split evenly over waves");
+    static_assert(BM % 8 == 0 && NINS % NW == 0 && IPW >= 1, "DMA ops split evenly over waves");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "tile");
-    static_assert(S >= 2 && S <= 4 && (ROWB == 64 || ROWB == 128), "ring");
+    static_assert(S >= 2 && S <= 8 && S * STAGE <= 152 * 1024, "ring (LDS also holds the tile tables)");
 };
 
-// Byte offset of logical 16-byte chunk kc of staged row `row`.  64-byte rows:
-// chunk kc ^ ((row >> 1) & 3); 128-byte rows: chunk kc ^ (row & 7).  Both were
-// measured free of bank conflicts on gfx950 for the fragment reads (16 rows x
-// 4 chunks per ds_read_b128) and for the 1 KB DMA writes.
-template <int ROWB>
-__device__ __forceinline__ int dma_off(int row, int kc)
+// Byte offset of logical 16-byte chunk kc of a staged 128-byte row: chunk
+// kc ^ (row & 7), measured free of bank conflicts on gfx950 for the fragment
+// reads (16 rows x 4 chunks per ds_read_b128) and for the 1 KB DMA writes.
+__device__ __forceinline__ int dma_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
+
+// Same for a 64-byte fp8 weight row: chunk kc ^ ((row >> 2) & 3), so that the
+// 8-byte fragment reads of 16 consecutive rows spread over all banks.
+__device__ __forceinline__ int dma_off_w8(int row, int kc) { return row * 64 + ((kc ^ ((row >> 2) & 3)) << 4); }
+
+// Eight e4m3 codes -> eight bf16 (exact), two per conversion: the scale
+// operand of this conversion acts through its exponent only, so 1.0.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1)
 {
-    if (ROWB == 64) return row * 64 + ((kc ^ ((row >> 1) & 3)) << 4);
-    return row * 128 + ((kc ^ (row & 7)) << 4);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return u32x4_t{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
 }
+
+// vmcnt <= n for a wave-uniform runtime n in [0, MAX]
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_le(int n);
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -515,6 +551,15 @@ __device__ __forceinline__ void wait_vmcnt()
     static_assert(N >= 0 && N < 64, "vmcnt");
     // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_le(int n)
+{
+    if constexpr (MAX > 0) {
+        if (n < MAX) { wait_vmcnt_le<MAX - 1>(n); return; }
+    }
+    wait_vmcnt<MAX>();
 }
 
 // One 16-byte-per-lane global->LDS transfer into the 1 KB at LDS byte address
@@ -586,22 +631,31 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     if (tile >= total) return;
 
     const int nk = a.K / C::BK;
-    const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * 2;
+    const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * (C::W8 ? 1 : 2);
     const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds;
-    // this lane's row within a DMA op and the logical chunk it fetches (the op
-    // writes lane l's 16 bytes at byte 16*l: row l / (ROWB/16), physical chunk
-    // l % (ROWB/16), which holds logical chunk physical ^ swizzle(row))
-    const int lrow = (C::ROWB == 64) ? (lane >> 2) : (lane >> 3);
-    const int lchunk = (C::ROWB == 64) ? ((lane & 3) ^ ((lane >> 3) & 3)) : ((lane & 7) ^ (lane >> 3));
 
-    // Source row of this lane for op q of tile ti: op q of this wave stages
-    // rows [RPO*(q*NW + wave), +RPO); rows < BM are A rows, the rest B rows.
+    // Op o = q*NW + wave of a stage (wave-uniform) stages activation rows
+    // 8o .. 8o+7 when o < A_OPS, else weight rows: 8 bf16 or 16 fp8 rows from
+    // row (o - A_OPS) * rows-per-op.  Lane l writes the op's LDS bytes
+    // [16l, 16l+16): row l / 8 (l / 4 for fp8 rows) of the op, physical chunk
+    // l % 8 (l % 4), which holds logical chunk physical ^ swizzle(row).
+    auto op_is_a = [&](int q) { return q * C::NW + wave < C::A_OPS; };
+    auto op_row = [&](int q) {  // A row, or B row, of this lane in op q
+        const int o = q * C::NW + wave;
+        if (o < C::A_OPS) return o * 8 + (lane >> 3);
+        return C::W8 ? (o - C::A_OPS) * 16 + (lane >> 2) : (o - C::A_OPS) * 8 + (lane >> 3);
+    };
+    auto op_chunk = [&](int q, int row) {  // logical 16-byte chunk this lane fetches
+        if (op_is_a(q) || !C::W8) return (lane & 7) ^ (row & 7);
+        return (lane & 3) ^ ((row >> 2) & 3);
+    };
+
     // For FC1 A rows the token comes from permuted_pair: a_raw() only loads the
     // entry (from an always-valid address) and source() interprets it, so the
     // next tile's loads can be issued early and consumed a whole tile later.
     auto a_raw = [&](const TileInfo& ti, int q) -> int {
-        const int row = (q * C::NW + wave) * C::RPO + lrow;
-        if (MODE == FC2 || row >= C::BM) return 0;
+        const int row = op_row(q);
+        if (MODE == FC2 || !op_is_a(q)) return 0;
         const int rr = ti.m0 + row;
         const int i = (ti.g < a.E && rr < ti.nrows) ? ti.row0 + rr : 0;
         // global-space load: a flat load would also count in lgkmcnt and make
@@ -609,9 +663,9 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         return *(const __attribute__((address_space(1))) int*)(a.permuted_pair + i);
     };
     auto source = [&](const TileInfo& ti, int q, int raw) -> const char* {
-        const int row = (q * C::NW + wave) * C::RPO + lrow;
+        const int row = op_row(q);
         const char* p;
-        if (row < C::BM) {
+        if (op_is_a(q)) {
             const int rr = ti.m0 + row;
             long r;
             if (MODE == FC1) {
@@ -622,7 +676,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             }
             p = a.a_src + (size_t)r * a_ld;
         } else {
-            const int j = row - C::BM;
+            const int j = row;
             int wrow;
             if (MODE == FC1) {
                 const int blk = j >> 4, pair = blk >> 1;
@@ -633,20 +687,18 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             }
             p = a.w + ((size_t)ti.g * a.N + wrow) * w_ld;
         }
-        return p + lchunk * 16;
+        return p + op_chunk(q, row) * 16;
     };
     const char* src[C::IPW];
     auto issue = [&](int st, int kt) {
 #pragma unroll
         for (int q = 0; q < C::IPW; ++q)
             dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + (q * C::NW + wave) * 1024),
-                  src[q] + (size_t)kt * C::ROWB);
+                  src[q] + (size_t)kt * (op_is_a(q) ? 128 : C::BROWB));
     };
-    auto wait_stage = [&](int later) {  // this wave's slice with `later` newer slices in flight has landed
-        if (later >= 2) wait_vmcnt<2 * C::IPW>();
-        else if (later == 1) wait_vmcnt<C::IPW>();
-        else wait_vmcnt<0>();
-    };
+    // this wave's transfers of a slice have landed while `later` newer slices'
+    // transfers (IPW each) may still be in flight
+    auto wait_stage = [&](int later) { wait_vmcnt_le<(C::S - 2) * C::IPW>(later * C::IPW); };
 
     TileInfo cur = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
     {
@@ -673,31 +725,81 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         }
 
         f32x4_t acc[C::MI][C::NI];
+        f32x4_t part[C::W8 ? C::MI : 1][C::W8 ? C::NI : 1];  // fp8: this K block's sums
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (C::W8) {
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) part[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 
         for (int kt = 0; kt < nk; ++kt) {
             wait_stage(min(C::S - 2, nk - 1 - kt));
             lds_barrier();  // slice kt is in LDS for every wave; slot of slice kt-1 is free
             if (kt + C::S - 1 < nk) issue((ring + kt + C::S - 1) % C::S, kt + C::S - 1);
             const char* la = lds + ((ring + kt) % C::S) * C::STAGE;
-            const char* lb = la + C::BM * C::ROWB;
+            const char* lb = la + C::A_BYTES;
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
                 const int kc = ks * 4 + (lane >> 4);
                 u32x4_t fa[C::MI], fb[C::NI];
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
-                    fa[mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off<C::ROWB>(wm * C::WTM + mi * 16 + (lane & 15), kc));
+                    fa[mi] = *reinterpret_cast<const u32x4_t*>(la + dma_off(wm * C::WTM + mi * 16 + (lane & 15), kc));
 #pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni)
-                    fb[ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off<C::ROWB>(wn * C::WTN + ni * 16 + (lane & 15), kc));
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    const int row = wn * C::WTN + ni * 16 + (lane & 15);
+                    if constexpr (C::W8) {
+                        // 8 fp8 values at K = 32*ks + 8*(lane/16): byte 8*(4*ks + lane/16)
+                        // of the 64-byte row, in 16-byte chunk 2*ks + lane/32
+                        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(
+                            lb + dma_off_w8(row, ks * 2 + (lane >> 5)) + ((lane >> 4) & 1) * 8);
+                        fb[ni] = fp8x8_to_bf16x8(w.x, w.y);
+                    } else {
+                        fb[ni] = *reinterpret_cast<const u32x4_t*>(lb + dma_off(row, kc));
+                    }
+                }
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+                    for (int ni = 0; ni < C::NI; ++ni) {
+                        if constexpr (C::W8) part[mi][ni] = mfma_frag(fa[mi], fb[ni], part[mi][ni], bf16_t());
+                        else acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+                    }
+            }
+            if constexpr (C::W8) {
+                if (kt & 1) {
+                    // end of a 128-wide K block: acc += block scale * partial.  The
+                    // scale index is wave-uniform; the constant address space makes
+                    // the loads scalar, so they do not count against the
+                    // transfers' vmcnt.
+                    const int kb = kt >> 1, sk = a.K / 128;
+                    const __attribute__((address_space(4))) float* ws =
+                        (const __attribute__((address_space(4))) float*)a.wscale;
+#pragma unroll
+                    for (int ni = 0; ni < C::NI; ++ni) {
+                        const int j = wn * C::WTN + ni * 16;  // first weight row of this block
+                        int wrow;
+                        if (MODE == FC1) {
+                            const int blk = j >> 4, pair = blk >> 1;
+                            const int col = cur.nt * (C::BN / 2) + pair * 16;
+                            wrow = (blk & 1) ? a.I + col : col;
+                        } else {
+                            wrow = min(cur.nt * C::BN + j, a.N - 1);
+                        }
+                        const float sc = ws[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kb];
+#pragma unroll
+                        for (int mi = 0; mi < C::MI; ++mi) {
+                            acc[mi][ni] += sc * part[mi][ni];
+                            part[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+                }
             }
         }
 
@@ -829,21 +931,36 @@ moe_status run_classes(const FfnArgs& f, int R, hipStream_t s, int kid)
     return run_gemm<AT, WT, MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
 }
 
-// bf16 activations and weights: mid and big groups on the direct-to-LDS engine.
-template <int MODE>
-moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
+// bf16 activations with bf16 or fp8 weights: every row class on the
+// direct-to-LDS engine.
+template <int MODE, class Skinny, class Mid, class Big>
+moe_status run_classes_dma(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-    // shapes chosen by measurement on MI355X: 4 waves per SIMD for the large
-    // tiles (one wave alone cannot keep the MFMA pipe busy), 128-byte K slices
-    // (whole-line requests), a deeper ring for the weight-streaming skinny tiles
-    using Skinny = DmaCfg<32, 256, 1, 4, 2, 4>;
-    using Mid = DmaCfg<128, 256, 4, 4, 2, 3>;
-    using Big = DmaCfg<256, 256, 4, 4, 4, 2>;
     moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid);
     if (st != MOE_OK) return st;
     st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
     if (st != MOE_OK) return st;
     return run_dma_gemm<MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
+}
+
+// Shapes chosen by measurement on MI355X: 4 waves per SIMD for the large tiles
+// (one wave alone cannot keep the MFMA pipe busy), whole-line requests, a
+// deeper ring for the weight-streaming skinny tiles.
+template <int MODE>
+moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
+{
+    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 4>, DmaCfg<128, 256, 4, 4, 2, 3>,
+                           DmaCfg<256, 256, 4, 4, 4, 2>>(f, R, s, kid);
+}
+
+// fp8 weights keep a second (per-scale-block) accumulator set, which does not
+// fit a 256x256 tile's registers: big groups use the 128x256 shape too.  Half
+// as many weight bytes per stage allow deeper rings.
+template <int MODE>
+moe_status run_classes_w8(const FfnArgs& f, int R, hipStream_t s, int kid)
+{
+    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 6, true>, DmaCfg<128, 256, 4, 4, 2, 4, true>,
+                           DmaCfg<128, 256, 4, 4, 4, 4, true>>(f, R, s, kid);
 }
 
 template <class AT, class WT>
@@ -861,6 +978,16 @@ moe_status run_ffn<bf16_t, bf16_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R
     if (st != MOE_OK) return st;
     return run_classes_bf16<FC2>(fc2, R, s, MOE_KID_FC2);
 }
+
+#ifndef MOE_FP8_REGISTER_ENGINE
+template <>
+moe_status run_ffn<bf16_t, fp8_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
+{
+    moe_status st = run_classes_w8<FC1>(fc1, R, s, MOE_KID_FC1);
+    if (st != MOE_OK) return st;
+    return run_classes_w8<FC2>(fc2, R, s, MOE_KID_FC2);
+}
+#endif
 
 // fp32 (small reference-precision layers): one 32x128 tile shape for all groups.
 template <>
