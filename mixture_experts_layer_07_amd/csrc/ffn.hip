@@ -954,13 +954,14 @@ moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
 }
 
 // fp8 weights keep a second (per-scale-block) accumulator set, which does not
-// fit a 256x256 tile's registers: big groups use the 128x256 shape too.  Half
-// as many weight bytes per stage allow deeper rings.
+// fit a 256x256 tile's registers: big groups use the 128x256 shape too, with
+// 8 waves of 64x64 (fewer LDS bytes per MFMA than 16 waves of 32x64: -4%
+// time measured).  Half as many weight bytes per stage allow deeper rings.
 template <int MODE>
 moe_status run_classes_w8(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 6, true>, DmaCfg<128, 256, 4, 4, 2, 4, true>,
-                           DmaCfg<128, 256, 4, 4, 4, 4, true>>(f, R, s, kid);
+    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 6, true>, DmaCfg<128, 256, 2, 4, 2, 4, true>,
+                           DmaCfg<128, 256, 2, 4, 4, 4, true>>(f, R, s, kid);
 }
 
 template <class AT, class WT>
