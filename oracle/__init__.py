@@ -14,7 +14,7 @@ import numpy as np
 from . import build as _build
 
 F32, BF16, FP8 = 0, 1, 2
-DEFAULT, RENORMALIZE, DEEPSEEKV3, RENORMALIZE_NAIVE = 0, 1, 2, 4
+DEFAULT, RENORMALIZE, DEEPSEEKV3, LLAMA4, RENORMALIZE_NAIVE, MINIMAX2, SIGMOID_RENORM = 0, 1, 2, 3, 4, 5, 6
 DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8}
 
 _lib = None

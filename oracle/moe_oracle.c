@@ -10,7 +10,10 @@
  *         formula y = sum_{i in TopK(x)} g_i(x) E_i(x) and the shared expert),
  *         "路由方法枚举" (RoutingMethodType comments), "DeepSeek-V3 的 noaux_tc"
  *         (sigmoid, bias for selection only, top-2 group sums, group mask,
- *         unbiased renormalisation + 1e-20 + routed scaling factor),
+ *         unbiased renormalisation + 1e-20 + routed scaling factor; the
+ *         Llama4 "Top1 -> Sigmoid", MiniMaxM2 "Sigmoid -> RoutingBiasAdd ->
+ *         TopK -> Renormalize(without bias)" and SigmoidRenorm "Sigmoid ->
+ *         TopK -> Renormalize" comments of the enum),
  *         "权重加载" (fused gate/up projection, gated activation expands FC1
  *         to 2*I), "小结" (FC1 -> act -> FC2 then apply weights / finalize).
  *  [VLLM] "vLLM 源码完全拆解(八): MoE 层的前向执行", sections "FusedTopKRouter"
@@ -33,6 +36,11 @@
  *  - Default honours an explicit renormalise flag (vLLM FusedTopKRouter).
  *  - The 1e-20 guard applies to DeepSeek-V3 only; the routed scaling factor
  *    multiplies every method's scales (1.0 unless given).
+ *  - Llama4: the k largest logits (the name fixes k = 1; larger k keeps the
+ *    same rule), each weighted by its own sigmoid, no renormalisation.
+ *  - MiniMax2 / SigmoidRenorm select on the same fp32 keys as DeepSeek-V3
+ *    with one group (fl32 sigmoid, plus the bias for MiniMax2 only) and
+ *    divide the chosen unbiased sigmoids by their sum.
  *  - w13 rows [0, I) are the gate projection, rows [I, 2I) the up projection;
  *    SwiGLU h = silu(gate) * up with silu(z) = z / (1 + exp(-z)).
  *  - fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of
@@ -179,7 +187,26 @@ static void route_token(const float* l, int E, int method, int k, int n_group,
         return;
     }
 
-    /* softmax family: the top-k set is selected on the fp32 logits */
+    if (method == ORACLE_MINIMAX2 || method == ORACLE_SIGMOID_RENORM) {
+        /* sigmoid scores; MiniMax2 adds the bias to the selection key only */
+        for (int e = 0; e < E; ++e) {
+            sig[e] = oracle_sigmoid_f32(l[e], hard);
+            c[e].key = (method == ORACLE_MINIMAX2 && bias) ? sig[e] + bias[e] /* one fp32 add */
+                                                           : sig[e];
+            c[e].idx = e;
+        }
+        qsort(c, (size_t)E, sizeof(cand_t), cand_cmp);
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j)
+            sum += (double)sig[c[j].idx];
+        for (int j = 0; j < k; ++j) {
+            ids[j] = c[j].idx;
+            scales[j] = (double)sig[c[j].idx] / sum * scaling;
+        }
+        return;
+    }
+
+    /* softmax family and Llama4: the top-k set is selected on the fp32 logits */
     for (int e = 0; e < E; ++e) {
         c[e].key = l[e];
         c[e].idx = e;
@@ -188,6 +215,12 @@ static void route_token(const float* l, int E, int method, int k, int n_group,
     for (int j = 0; j < k; ++j)
         ids[j] = c[j].idx;
 
+    if (method == ORACLE_LLAMA4) {
+        /* Top1 -> Sigmoid: each kept expert weighs its own sigmoid */
+        for (int j = 0; j < k; ++j)
+            scales[j] = 1.0 / (1.0 + exp(-(double)c[j].key)) * scaling;
+        return;
+    }
     if (method == ORACLE_RENORMALIZE) {
         /* TopK -> Softmax over the selected logits only */
         double m = (double)c[0].key, z = 0.0;
@@ -225,7 +258,8 @@ int oracle_route(const float* logits, int T, int E, int method, int k, int n_gro
             E / n_group < 2 || k > topk_group * (E / n_group))
             return -1;
     } else if (method != ORACLE_DEFAULT && method != ORACLE_RENORMALIZE &&
-               method != ORACLE_RENORMALIZE_NAIVE) {
+               method != ORACLE_RENORMALIZE_NAIVE && method != ORACLE_LLAMA4 &&
+               method != ORACLE_MINIMAX2 && method != ORACLE_SIGMOID_RENORM) {
         return -1;
     }
     cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)E);

@@ -15,7 +15,10 @@ enum {
     ORACLE_DEFAULT = 0,
     ORACLE_RENORMALIZE = 1,
     ORACLE_DEEPSEEKV3 = 2,
-    ORACLE_RENORMALIZE_NAIVE = 4
+    ORACLE_LLAMA4 = 3,
+    ORACLE_RENORMALIZE_NAIVE = 4,
+    ORACLE_MINIMAX2 = 5,
+    ORACLE_SIGMOID_RENORM = 6
 };
 
 typedef struct {

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from pins import (brute_group_score, brute_topk, ordered_by_key, sigmoid_f32_exact)
+from pins import (brute_group_score, brute_topk, ordered_by_key, sigmoid_decimal,
+                  sigmoid_f32_exact)
 
 GRID = np.array([-2, -1, 0, 1, 2], np.float32) / np.float32(4)  # tie-heavy, exact in fp32
 
@@ -174,6 +175,75 @@ def test_dsv3_bias_only_selects(orc):
     np.testing.assert_allclose(sc[0], [s3 / (s3 + 0.5), 0.5 / (s3 + 0.5)], rtol=1e-13)
 
 
+# ------------------------------------------- sigmoid family without grouping
+def sigmoid_reference(lg, bias, k, scaling):
+    """MiniMax2 / SigmoidRenorm by enumeration: decimal sigmoid rounded to fp32,
+    optional bias added in fp32 for the key, unbiased sigmoids renormalised."""
+    out = []
+    for row in lg:
+        sig = [sigmoid_f32_exact(float(v)) for v in row]
+        kap = [np.float32(sig[e] + np.float32(bias[e])) if bias is not None else sig[e]
+               for e in range(len(row))]
+        S = brute_topk([float(v) for v in kap], k)
+        den = sum(float(sig[e]) for e in S)
+        out.append((S, kap, {e: float(sig[e]) / den * scaling for e in S}))
+    return out
+
+
+@pytest.mark.parametrize("E", [4, 6, 8, 12])
+@pytest.mark.parametrize("use_bias", [True, False])
+def test_sigmoid_methods_brute_force(orc, E, use_bias):
+    """MiniMax2 (sigmoid, bias for selection, renormalise without bias) and
+    SigmoidRenorm (sigmoid, top-k, renormalise), RoutingMethodType comments."""
+    rng = np.random.default_rng(300 + E + 50 * use_bias)
+    method = orc.MINIMAX2 if use_bias else orc.SIGMOID_RENORM
+    for k in range(1, E + 1):
+        lg = tie_logits(rng, 3, E)
+        bias = (rng.choice(GRID, size=E) / np.float32(2)).astype(np.float32) if use_bias else None
+        ids, sc, hard = orc.route(lg, k, method, 1, 1, bias, 1.5)
+        assert hard == 0
+        for t, (S, kap, w) in enumerate(sigmoid_reference(lg, bias, k, 1.5)):
+            assert tuple(sorted(ids[t])) == S, (E, k, t)
+            assert ordered_by_key(list(ids[t]), [float(v) for v in kap])
+            for j, e in enumerate(ids[t]):
+                assert sc[t, j] == pytest.approx(w[e], rel=1e-13)
+        assert np.allclose(sc.sum(1), 1.5, rtol=1e-13)
+
+
+def test_sigmoid_methods_equal_single_group_dsv3(orc):
+    """MiniMax2 is DeepSeek-V3's rule with one group (equal up to DeepSeek-V3's
+    1e-20 guard), and SigmoidRenorm is MiniMax2 with a zero bias."""
+    rng = np.random.default_rng(9)
+    lg = rng.standard_normal((64, 32)).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 32).astype(np.float32)
+    a = orc.route(lg, 6, orc.MINIMAX2, 1, 1, bias, 2.5)
+    b = orc.route(lg, 6, orc.DEEPSEEKV3, 1, 1, bias, 2.5)
+    assert np.array_equal(a[0], b[0])
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-13)
+    c = orc.route(lg, 6, orc.SIGMOID_RENORM, 1, 1, None, 2.5)
+    d = orc.route(lg, 6, orc.MINIMAX2, 1, 1, np.zeros(32, np.float32), 2.5)
+    assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1])
+
+
+@pytest.mark.parametrize("E", [4, 8, 12])
+def test_llama4_brute_force(orc, E):
+    """Llama4: top-1 (and, by the same rule, top-k) on the logits, each kept
+    expert weighted by its own sigmoid (decimal reference), no renormalisation."""
+    rng = np.random.default_rng(400 + E)
+    for k in (1, 2, E):
+        lg = tie_logits(rng, 4, E)
+        ids, sc, _ = orc.route(lg, k, orc.LLAMA4, 1, 1, None, 1.0)
+        for t in range(lg.shape[0]):
+            keys = [float(v) for v in lg[t]]
+            assert tuple(sorted(ids[t])) == brute_topk(keys, k)
+            assert ordered_by_key(list(ids[t]), keys)
+            for j, e in enumerate(ids[t]):
+                assert sc[t, j] == pytest.approx(float(sigmoid_decimal(keys[e])), rel=1e-14)
+    lg = np.array([[0.0, 3.0, -1.0, 3.0]], np.float32)
+    ids, sc, _ = orc.route(lg, 1, orc.LLAMA4, 1, 1, None, 1.0)
+    assert ids.tolist() == [[1]] and sc[0, 0] == pytest.approx(1 / (1 + math.exp(-3.0)), rel=1e-15)
+
+
 def test_handworked_golden(orc):
     """Hand-derived routing examples (derivations in the fixture file)."""
     path = os.path.join(os.path.dirname(__file__), "golden", "route_handworked.json")
@@ -198,3 +268,5 @@ def test_rejects_invalid(orc):
         orc.route(lg, 2, orc.DEEPSEEKV3, 3, 1)   # 8 % 3 != 0
     with pytest.raises(ValueError):
         orc.route(lg, 5, orc.DEEPSEEKV3, 4, 2)   # k > topk_group * group size
+    with pytest.raises(ValueError):
+        orc.route(lg, 2, 7)                      # DeepSeekV4: not defined on the pages
