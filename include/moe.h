@@ -56,8 +56,14 @@ typedef enum moe_route_method {
     MOE_ROUTE_DEFAULT = 0,           /* softmax over all E -> top-k          */
     MOE_ROUTE_RENORMALIZE = 1,       /* top-k -> softmax over the k kept     */
     MOE_ROUTE_DEEPSEEKV3 = 2,        /* noaux_tc grouped sigmoid routing     */
-    MOE_ROUTE_RENORMALIZE_NAIVE = 4  /* softmax -> top-k -> renormalise      */
+    MOE_ROUTE_LLAMA4 = 3,            /* top-k logits -> own sigmoid each     */
+    MOE_ROUTE_RENORMALIZE_NAIVE = 4, /* softmax -> top-k -> renormalise      */
+    MOE_ROUTE_MINIMAX2 = 5,          /* sigmoid + bias -> top-k -> renormalise
+                                        the unbiased sigmoids                 */
+    MOE_ROUTE_SIGMOID_RENORM = 6     /* sigmoid -> top-k -> renormalise      */
 } moe_route_method;
+/* 7 (DeepSeek-V4) and 8 (unspecified) are listed by the enum but not defined
+ * on the pages: MOE_ERR_UNSUPPORTED. */
 
 /* Honoured by MOE_ROUTE_DEFAULT only: divide the k kept probabilities by their
  * sum (the renormalize switch of vLLM's FusedTopKRouter). */
@@ -84,18 +90,22 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype
  *           two largest biased keys; the topk_group best groups are kept and
  *           the k experts are chosen among them (k <= topk_group * E/n_group).
  *           Ignored by the other methods.
- *  bias     device fp32 [E] or NULL (= zeros); DeepSeek-V3 only: added to the
- *           sigmoid scores for selection, never to the weights.
+ *  bias     device fp32 [E] or NULL (= zeros); DeepSeek-V3 and MiniMax2 only:
+ *           added to the sigmoid scores for selection, never to the weights.
  *  scaling  multiplies every returned scale (routed scaling factor; pass 1.0
  *           when the model has none).
  *  flags    MOE_ROUTE_FLAG_RENORMALIZE (DEFAULT only).
  *  ids      device int32 [T, k] out: chosen experts, ordered by key
  *           descending, ties to the lower expert index (groups likewise).
  *  scales   device fp32 [T, k] out: weights of `ids`, same order.
- * Selection precision: softmax methods select on the fp32 logits (softmax is
- * monotone); DeepSeek-V3 selects on fl32(sigmoid) + bias with the sigmoid
- * evaluated in fp64 and rounded once to fp32.  Weights are computed in fp64
- * and rounded once.  NaN logits give unspecified (but in-bounds) ids.
+ * Selection precision: softmax methods and Llama4 select on the fp32 logits
+ * (softmax is monotone); DeepSeek-V3, MiniMax2 and SigmoidRenorm select on
+ * fl32(sigmoid) (+ bias) with the sigmoid evaluated in fp64 and rounded once
+ * to fp32.  Weights are computed in fp64 and rounded once: Llama4 weighs each
+ * kept expert by its own sigmoid (the name fixes k = 1; larger k keeps the
+ * rule); MiniMax2 and SigmoidRenorm divide the kept sigmoids by their sum
+ * (DeepSeek-V3 adds 1e-20 to that sum).  NaN logits give unspecified (but
+ * in-bounds) ids.
  */
 moe_status moe_route(const float* logits, int T, int E, int method, int k, int n_group,
                      int topk_group, const float* bias, float scaling, unsigned flags,

@@ -153,10 +153,9 @@ moe_status moe_route(const float* logits, int T, int E, int method, int k, int n
 {
     moe_status st = check_common(T, k, E, 0);
     if (st != MOE_OK) return st;
-    if (method == 3 || (method >= 5 && method <= 8))
-        return set_error(MOE_ERR_UNSUPPORTED, "routing method %d is not implemented (supported: 0, 1, 2, 4)", method);
-    if (method != MOE_ROUTE_DEFAULT && method != MOE_ROUTE_RENORMALIZE &&
-        method != MOE_ROUTE_DEEPSEEKV3 && method != MOE_ROUTE_RENORMALIZE_NAIVE)
+    if (method == 7 || method == 8)
+        return set_error(MOE_ERR_UNSUPPORTED, "routing method %d is not implemented (supported: 0-6)", method);
+    if (method < MOE_ROUTE_DEFAULT || method > MOE_ROUTE_SIGMOID_RENORM)
         return set_error(MOE_ERR_INVALID_ARG, "unknown routing method %d", method);
     if (flags & ~MOE_ROUTE_FLAG_RENORMALIZE)
         return set_error(MOE_ERR_INVALID_ARG, "unknown routing flags 0x%x", flags);
@@ -176,7 +175,8 @@ moe_status moe_route(const float* logits, int T, int E, int method, int k, int n
     if (!logits || !ids || !scales)
         return set_error(MOE_ERR_INVALID_ARG, "logits, ids and scales must be non-null");
     return launch_route(logits, T, E, method, k, n_group, topk_group,
-                        method == MOE_ROUTE_DEEPSEEKV3 ? bias : nullptr, scaling, flags, ids,
+                        (method == MOE_ROUTE_DEEPSEEKV3 || method == MOE_ROUTE_MINIMAX2) ? bias : nullptr,
+                        scaling, flags, ids,
                         scales, static_cast<hipStream_t>(stream));
 }
 

@@ -9,6 +9,10 @@
 //                      score = sum of the group's two best biased keys; keep
 //                      topk_group groups; top-k experts among them; weights
 //                      = unbiased sigmoid / (sum + 1e-20) * scaling.
+//   Llama4             top-k logits, each weighted by its own sigmoid
+//   MiniMax2           sigmoid + bias for selection, top-k, unbiased sigmoids
+//                      renormalised (DeepSeekV3 with one group, no 1e-20)
+//   SigmoidRenorm      sigmoid, top-k, renormalise
 //
 // Layout: lane l owns experts l, l+64, l+128, l+192 (E <= 256).  Selection
 // keys are packed into one 64-bit integer (order-preserving fp32 bits, then
@@ -86,6 +90,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int t = blockIdx.x * kWaves + wave;
     const bool active = t < T;
     const bool dsv3 = method == MOE_ROUTE_DEEPSEEKV3;
+    // sigmoid-scored methods select on fl32(sigmoid) (+ bias)
+    const bool sigm = dsv3 || method == MOE_ROUTE_MINIMAX2 || method == MOE_ROUTE_SIGMOID_RENORM;
 
     float logit[4], key[4];
     bool valid[4];
@@ -97,18 +103,20 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         key[i] = logit[i];
     }
 
-    if (dsv3) {
-        const int gsz = E / n_group;
+    if (sigm) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
             if (valid[i]) {
                 const float sg = sigmoid_key(logit[i]);
-                key[i] = sg + (bias ? bias[e] : 0.0f);  // one fp32 add
+                key[i] = bias ? sg + bias[e] : sg;  // one fp32 add (bias given: DSV3, MiniMax2)
                 s_sig[wave][e] = sg;
                 s_key[wave][e] = key[i];
             }
         }
+    }
+    if (dsv3) {
+        const int gsz = E / n_group;
         __syncthreads();
         // group score: sum of the two largest biased keys of the group
         if (active) {
@@ -176,13 +184,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     // weights, in fp64, rounded once
     double w[MOE_MAX_TOPK];
     double wsum = 0.0;
-    if (dsv3) {
+    if (sigm) {
 #pragma unroll
         for (int j = 0; j < MOE_MAX_TOPK; ++j) {
             w[j] = (j < k) ? (double)s_sig[wave][sel_id[j]] : 0.0;
             wsum += w[j];
         }
-        wsum += 1e-20;
+        if (dsv3) wsum += 1e-20;
+    } else if (method == MOE_ROUTE_LLAMA4) {
+        // the kept logits' own sigmoids, not renormalised
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK; ++j)
+            w[j] = (j < k) ? 1.0 / (1.0 + exp(-(double)sel_key[j])) : 0.0;
+        wsum = 1.0;
     } else {
         const double m = (double)sel_key[0];
 #pragma unroll

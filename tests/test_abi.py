@@ -61,7 +61,7 @@ def test_route_validation(L):
     assert r(p, 4, 8, 0, 0, 1, 1, None, 1.0, 0, p, p, None) == INVALID      # k = 0
     assert r(p, 4, 300, 0, 2, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED  # E > 256
     assert r(p, 4, 64, 0, 9, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED  # k > 8
-    assert r(p, 4, 8, 3, 2, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED   # Llama4
+    assert r(p, 4, 8, 7, 2, 1, 1, None, 1.0, 0, p, p, None) == UNSUPPORTED   # DeepSeekV4 (undefined)
     assert r(p, 4, 8, 9, 2, 1, 1, None, 1.0, 0, p, p, None) == INVALID       # unknown method
     assert r(p, 4, 8, 0, 2, 1, 1, None, 1.0, 2, p, p, None) == INVALID       # unknown flag
     assert r(p, 4, 8, 0, 2, 1, 1, None, float("inf"), 0, p, p, None) == INVALID

@@ -77,6 +77,8 @@ TIE_GRID = np.array([-2, -1, 0, 1, 2], np.float32) / np.float32(4)
     (8, 2, 0, 1, 1), (8, 8, 0, 1, 1), (64, 6, 1, 1, 1), (65, 3, 4, 1, 1), (256, 8, 4, 1, 1),
     (128, 8, 0, 1, 1), (256, 8, 2, 8, 4), (256, 1, 2, 8, 1), (64, 8, 2, 32, 4),
     (256, 8, 2, 128, 8), (96, 5, 2, 3, 2), (12, 4, 2, 6, 3), (256, 8, 2, 16, 16),
+    (8, 1, 3, 1, 1), (128, 4, 3, 1, 1), (64, 8, 5, 1, 1), (256, 8, 5, 1, 1),
+    (32, 4, 6, 1, 1), (256, 8, 6, 1, 1), (7, 7, 6, 1, 1),
 ])
 @pytest.mark.parametrize("ties", [True, False])
 def test_route_parity_fuzz(E, k, method, n_group, topk_group, ties):
@@ -90,7 +92,7 @@ def test_route_parity_fuzz(E, k, method, n_group, topk_group, ties):
         bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
     w = wl.Workload("fuzz", 98, T=T, H=128, E=E, I=128, k=k, method=method,
                     flags=int(rng.integers(0, 2)), n_group=n_group, topk_group=topk_group,
-                    scaling=float(rng.choice([1.0, 2.5])), bias=method == 2)
+                    scaling=float(rng.choice([1.0, 2.5])), bias=method in (2, 5))
     check_route(w, torch.from_numpy(logits), torch.from_numpy(bias) if w.bias else None)
 
 
@@ -104,10 +106,11 @@ def test_route_special_values():
     logits[3] = -1e-30
     logits[4] = np.float32(3.4e38) * np.sign(np.arange(E) - 31.5)
     logits[5:] = np.random.default_rng(0).standard_normal((3, E)) * 30
-    for method, ng, tg in [(0, 1, 1), (1, 1, 1), (4, 1, 1), (2, 8, 4), (2, 1, 1)]:
+    for method, ng, tg in [(0, 1, 1), (1, 1, 1), (4, 1, 1), (2, 8, 4), (2, 1, 1), (3, 1, 1),
+                           (5, 1, 1), (6, 1, 1)]:
         w = wl.Workload("special", 97, T=8, H=128, E=E, I=128, k=8, method=method,
-                        n_group=ng, topk_group=tg, bias=method == 2)
-        bias = torch.zeros(E) if method == 2 else None
+                        n_group=ng, topk_group=tg, bias=method in (2, 5))
+        bias = torch.zeros(E) if method in (2, 5) else None
         check_route(w, torch.from_numpy(logits), bias)
 
 
