@@ -298,6 +298,49 @@ def test_layer_nan_poisoned_buffers_and_determinism():
     assert rel_l2(host(outs[0]).double().numpy(), ref) < 1e-2
 
 
+@pytest.mark.parametrize("wdt", ["bf16", "fp8"])
+def test_layer_graph_capture_replays(wdt):
+    """The four calls captured into one HIP graph (no allocation, no host
+    readback, no memset inside) replay to the eager result, bit for bit, also
+    after the captured input buffers are refilled between replays."""
+    w = small_workload("bf16", wdt, T=700, E=16, k=4, n_shared=1, method=2, n_group=4,
+                       topk_group=2, scaling=2.5, bias=True)
+    layer = moe.layer_for_workload(w, DEV)
+    inputs = [{k: (None if v is None else v.to(DEV)) for k, v in wl.make_inputs(w, s).items()}
+              for s in (11, 12)]
+    g = {k: (None if v is None else v.clone()) for k, v in inputs[0].items()}  # captured buffers
+    fwd = lambda: layer(g["x"], g["logits"], g["w13"], g["w2"], g["bias"],  # noqa: E731
+                        g["w13_scale"], g["w2_scale"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y_graph = fwd()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = inputs[rep % 2]
+        for k, v in src.items():
+            if v is not None:
+                g[k].copy_(v)
+        torch.cuda.synchronize()
+        eager = layer(src["x"], src["logits"], src["w13"], src["w2"], src["bias"],
+                      src["w13_scale"], src["w2_scale"]).clone()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph.view(torch.int16), eager.view(torch.int16)), rep
+    ids, sc, _ = oracle_route(w, host(inputs[1]["logits"]), host(inputs[1]["bias"]))
+    W = oracle.Weights(host(g["w13"]), host(g["w2"]), wdt,
+                       None if g["w13_scale"] is None else host(g["w13_scale"]),
+                       None if g["w2_scale"] is None else host(g["w2_scale"]))
+    toks = np.arange(0, w.T, 7, dtype=np.int32)
+    ref = oracle.layer_tokens(W, host(inputs[1]["x"]), "bf16", w.T, w.k, w.E, 1, ids, sc, toks)
+    assert rel_l2(host(y_graph).double().numpy()[toks], ref) < TOL[("bf16", wdt)]
+
+
 def test_zero_tokens_is_noop():
     w = small_workload("bf16", "bf16", T=0, E=8, k=2)
     L = moe.lib()
