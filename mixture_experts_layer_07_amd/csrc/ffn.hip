@@ -944,12 +944,13 @@ moe_status run_classes_dma(const FfnArgs& f, int R, hipStream_t s, int kid)
 }
 
 // Shapes chosen by measurement on MI355X: 4 waves per SIMD for the large tiles
-// (one wave alone cannot keep the MFMA pipe busy), whole-line requests, a
-// deeper ring for the weight-streaming skinny tiles.
+// (one wave alone cannot keep the MFMA pipe busy), whole-line requests, and for
+// the weight-streaming skinny tiles a narrow 32x128 tile with a 6-deep ring
+// (5 slices, 100 KB, in flight per CU).
 template <int MODE>
 moe_status run_classes_bf16(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 4>, DmaCfg<128, 256, 4, 4, 2, 3>,
+    return run_classes_dma<MODE, DmaCfg<32, 128, 1, 4, 2, 6>, DmaCfg<128, 256, 4, 4, 2, 3>,
                            DmaCfg<256, 256, 4, 4, 4, 2>>(f, R, s, kid);
 }
 
