@@ -19,21 +19,17 @@
 // each round XCD x takes one contiguous slice of the list, so the M-tiles that
 // share a weight tile run together on the same XCD and share its L2.
 //
-// Tile engine.  Both operands are K-contiguous (activation rows and weight
-// rows), staged through LDS in 128-byte K slices (64 bf16 or 32 fp32 values
-// per row) whose 16-byte chunks are XOR-swizzled by row (conflict-free).
-// Double-buffered LDS with one barrier per K slice; the next slice's global
-// loads are in flight while MFMAs run on the current one.
-//   bf16:  v_mfma_f32_16x16x32_bf16; a lane feeds 8 consecutive K values of one
-//          row of A and of B.
-//   fp32:  v_mfma_f32_16x16x4f32, four per 16-byte fragment (lane group q
-//          feeds K = 4q + i to the i-th MFMA, the same for A and B, so the
-//          four products cover the 16 K values once).
-//   fp8 weights: codes are widened to bf16 while being staged into LDS (exact:
-//          every e4m3 value is a bf16 value); the fp32 block scale (one per
-//          128x128 block) is constant over each 128-wide K block, so each K
-//          block accumulates unscaled into a partial tile which is then added
-//          with its scale.
+// Two tile engines.  Both operands are K-contiguous (activation rows and
+// weight rows), staged through LDS in 128-byte K slices whose 16-byte chunks
+// are XOR-swizzled by row (conflict-free).
+//   Register-staged engine (fp32 layers): global -> VGPR -> LDS, double
+//          buffered, one barrier per slice; v_mfma_f32_16x16x4f32, four per
+//          16-byte fragment (lane group q feeds K = 4q + i to the i-th MFMA,
+//          the same for A and B, so the four products cover the 16 K values
+//          once).
+//   Direct-to-LDS engine (bf16 activations, bf16 or fp8 weights): described
+//          at DmaCfg below; v_mfma_f32_16x16x32_bf16, a lane feeding 8
+//          consecutive K values of one row of A and of B.
 // FC1 keeps the gate and up halves of an output column in the same lane: the
 // staged B tile alternates 16 gate rows and the matching 16 up rows, so MFMA
 // column blocks 2q and 2q+1 are gate and up of the same 16 outputs and the
@@ -78,20 +74,19 @@ struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_;
     static constexpr int NT = WM * WN * 64;
     static constexpr bool F32 = sizeof(AT) == 4;           // fp32 compute
-    static constexpr bool FP8 = sizeof(WT) == 1;
     static constexpr int ESZ = F32 ? 4 : 2;                 // LDS element size
     static constexpr int BK = kRowBytes / ESZ;              // K per slice
     static constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
     static constexpr int MI = WTM / 16, NI = WTN / 16;      // MFMA blocks
     static constexpr int A_CH = BM * (kRowBytes / 16) / NT; // 16-B A chunks / thread
-    static constexpr int B_GCH = FP8 ? 4 : 8;               // global 16-B chunks per B row
+    static constexpr int B_GCH = 8;                         // global 16-B chunks per B row
     static constexpr int B_CH = BN * B_GCH / NT;            // B chunks / thread
     static constexpr int LDS_A = BM * kLdsStride;
     static constexpr int LDS_B = BN * kLdsStride;
     static_assert(A_CH >= 1 && BM * 8 % NT == 0, "A tile too small for the block");
     static_assert(B_CH >= 1 && BN * B_GCH % NT == 0, "B tile too small for the block");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "wave tile");
-    static_assert(!FP8 || BK * 2 == 128 || BK == 128, "fp8 scale blocks");
+    static_assert(sizeof(AT) == sizeof(WT) && sizeof(WT) >= 2, "fp32 or bf16 operands");
 };
 
 __device__ __forceinline__ f32x4_t mfma_frag(u32x4_t a, u32x4_t b, f32x4_t c, bf16_t)
@@ -107,14 +102,6 @@ __device__ __forceinline__ f32x4_t mfma_frag(u32x4_t a, u32x4_t b, f32x4_t c, fl
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
     return c;
-}
-
-// Two OCP e4m3fn codes (low or high half of a 32-bit word) -> packed bf16 pair.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
-{
-    auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
 }
 
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
@@ -177,7 +164,7 @@ __device__ __forceinline__ void gload(u32x4_t (&ra)[C::A_CH], u32x4_t (&rb)[C::B
     for (int i = 0; i < C::B_CH; ++i) rb[i] = ldg16(b_ptr[i] + kb);
 }
 
-// Registers -> LDS buffer `buf` (fp8 weights widened to bf16 on the way).
+// Registers -> LDS buffer `buf`.
 template <class C>
 __device__ __forceinline__ void lstore(char* lds, const u32x4_t (&ra)[C::A_CH],
                                        const u32x4_t (&rb)[C::B_CH], int tid, int buf)
@@ -193,17 +180,7 @@ __device__ __forceinline__ void lstore(char* lds, const u32x4_t (&ra)[C::A_CH],
     for (int i = 0; i < C::B_CH; ++i) {
         const int c = tid + i * C::NT;
         const int j = c / C::B_GCH, q = c % C::B_GCH;
-        if (C::FP8) {
-            u32x4_t lo4, hi4;
-            lo4.x = fp8x2_to_bf16x2<false>(rb[i].x); lo4.y = fp8x2_to_bf16x2<true>(rb[i].x);
-            lo4.z = fp8x2_to_bf16x2<false>(rb[i].y); lo4.w = fp8x2_to_bf16x2<true>(rb[i].y);
-            hi4.x = fp8x2_to_bf16x2<false>(rb[i].z); hi4.y = fp8x2_to_bf16x2<true>(rb[i].z);
-            hi4.z = fp8x2_to_bf16x2<false>(rb[i].w); hi4.w = fp8x2_to_bf16x2<true>(rb[i].w);
-            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, 2 * q)) = lo4;
-            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, 2 * q + 1)) = hi4;
-        } else {
-            *reinterpret_cast<u32x4_t*>(lb + lds_off(j, q)) = rb[i];
-        }
+        *reinterpret_cast<u32x4_t*>(lb + lds_off(j, q)) = rb[i];
     }
 }
 
@@ -349,42 +326,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
         TileInfo nxt = cur;
 
         f32x4_t acc[C::MI][C::NI];
-        f32x4_t part[C::FP8 ? C::MI : 1][C::FP8 ? C::NI : 1];
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (C::FP8) {
-#pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni)
-                    part[C::FP8 ? mi : 0][C::FP8 ? ni : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
 
         for (int kt = 0; kt < nk; ++kt) {
-            // fp8: the block scales used at the end of this iteration are loaded
-            // before the next slice's loads, so that waiting for them does not
-            // also wait for those (loads complete in issue order)
-            const bool block_end = C::FP8 && ((kt + 1) * C::BK) % 128 == 0;
-            float bscale[C::FP8 ? C::NI : 1];
-            if (block_end) {
-                const int kb = (kt * C::BK) / 128;
-                const int sk = a.K / 128;
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) {
-                    const int j = wn * C::WTN + ni * 16;  // first staged B row of this block
-                    int wrow;
-                    if (MODE == FC1) {
-                        const int blk = j >> 4, pair = blk >> 1;
-                        const int col = cur.nt * (C::BN / 2) + pair * 16;
-                        wrow = (blk & 1) ? a.I + col : col;
-                    } else {
-                        wrow = min(cur.nt * C::BN + j, a.N - 1);
-                    }
-                    bscale[C::FP8 ? ni : 0] = a.wscale[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kb];
-                }
-            }
             // issue the next slice's loads: this tile's, or the next tile's first
             bool staged = true;
             if (kt + 1 < nk) {
@@ -412,25 +359,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < C::NI; ++ni) {
-                        if (C::FP8)
-                            part[C::FP8 ? mi : 0][C::FP8 ? ni : 0] =
-                                mfma_frag(fa[mi], fb[ni], part[C::FP8 ? mi : 0][C::FP8 ? ni : 0], CT());
-                        else
-                            acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], CT());
-                    }
-            }
-            if (block_end) {
-                // end of a 128-wide K block: acc += block scale * partial
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) {
-                    const float s = bscale[C::FP8 ? ni : 0];
-#pragma unroll
-                    for (int mi = 0; mi < C::MI; ++mi) {
-                        acc[mi][ni] += s * part[C::FP8 ? mi : 0][C::FP8 ? ni : 0];
-                        part[C::FP8 ? mi : 0][C::FP8 ? ni : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    }
-                }
+                    for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], CT());
             }
             if (staged) lstore<C>(lds, ra, rb, tid, buf ^ 1);
             __syncthreads();
@@ -916,21 +845,6 @@ constexpr int kMidRows = 64;
 constexpr int kBigRows = 384;
 constexpr int kAllRows = 1 << 30;
 
-template <class AT, class WT, int MODE>
-moe_status run_classes(const FfnArgs& f, int R, hipStream_t s, int kid)
-{
-    using Skinny = Cfg<AT, WT, 32, 128, 1, 4, 1>;
-    using Mid = Cfg<AT, WT, 128, 256, 2, 4, 2>;
-    // fp8 weights keep a second (per-scale-block) accumulator set, which does not
-    // fit a 256x256 tile's registers: they use the 128x256 shape for big groups
-    using Big = typename std::conditional<sizeof(WT) == 1, Mid, Cfg<AT, WT, 256, 256, 2, 4, 4>>::type;
-    moe_status st = run_gemm<AT, WT, MODE, Skinny>(f, 0, kMidRows, R, s, kid);
-    if (st != MOE_OK) return st;
-    st = run_gemm<AT, WT, MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
-    if (st != MOE_OK) return st;
-    return run_gemm<AT, WT, MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
-}
-
 // bf16 activations with bf16 or fp8 weights: every row class on the
 // direct-to-LDS engine.
 template <int MODE, class Skinny, class Mid, class Big>
@@ -966,12 +880,7 @@ moe_status run_classes_w8(const FfnArgs& f, int R, hipStream_t s, int kid)
 }
 
 template <class AT, class WT>
-moe_status run_ffn(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
-{
-    moe_status st = run_classes<AT, WT, FC1>(fc1, R, s, MOE_KID_FC1);
-    if (st != MOE_OK) return st;
-    return run_classes<AT, WT, FC2>(fc2, R, s, MOE_KID_FC2);
-}
+moe_status run_ffn(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s);
 
 template <>
 moe_status run_ffn<bf16_t, bf16_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
@@ -981,7 +890,6 @@ moe_status run_ffn<bf16_t, bf16_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R
     return run_classes_bf16<FC2>(fc2, R, s, MOE_KID_FC2);
 }
 
-#ifndef MOE_FP8_REGISTER_ENGINE
 template <>
 moe_status run_ffn<bf16_t, fp8_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
 {
@@ -989,7 +897,6 @@ moe_status run_ffn<bf16_t, fp8_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R,
     if (st != MOE_OK) return st;
     return run_classes_w8<FC2>(fc2, R, s, MOE_KID_FC2);
 }
-#endif
 
 // fp32 (small reference-precision layers): one 32x128 tile shape for all groups.
 template <>
