@@ -82,6 +82,21 @@ def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=Non
             "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
 
 
+def grouped_gemm_summary(w, touched, per_kernel):
+    """FC1 + FC2 together: the layer's expert-FFN FLOPs (real rows, not padded
+    tiles) and algorithmic bytes over the two GEMMs' time per step."""
+    f1, b1 = fc_work(w, touched, "fc1")
+    f2, b2 = fc_work(w, touched, "fc2")
+    ms = per_kernel["fc1"] + per_kernel["fc2"]
+    s = ms * 1e-3
+    peak_f = PEAK["f32" if w.act == "f32" else "bf16"]
+    return {"ms_per_step": round(ms, 4), "algorithmic_flops": f1 + f2,
+            "algorithmic_bytes": b1 + b2, "tflops": round((f1 + f2) / s / 1e12, 2),
+            "gbps": round((b1 + b2) / s / 1e9, 1),
+            "mfma_frac": round((f1 + f2) / s / 1e12 / peak_f, 4),
+            "hbm_frac": round((b1 + b2) / s / 1e9 / PEAK["hbm"], 4)}
+
+
 def load_traffic(workload):
     """HBM bytes per FC1 launch from the committed rocprofv3 counter summary,
     or None when the summary is missing or the kernel source changed since."""
@@ -276,6 +291,9 @@ def main():
                                f"{w.act} activations, {w.wdt} weights",
                    "global_batch": w.T, "parallelism": "single GPU, all experts local"},
         "roofline": rl,
+        "roofline_fc2": roofline(w, main_res["touched"], main_res["per_kernel"]["fc2"], "fc2",
+                                 launches=main_res["launches"]["fc2"]),
+        "grouped_gemm": grouped_gemm_summary(w, main_res["touched"], main_res["per_kernel"]),
         "per_kernel_ms": main_res["per_kernel"],
     }
     if not args.no_cpu_baseline:
@@ -295,6 +313,7 @@ def main():
                                  launches=d["launches"][DOMINANT]),
             "roofline_fc2": roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2",
                                      launches=d["launches"]["fc2"]),
+            "grouped_gemm": grouped_gemm_summary(dw, d["touched"], d["per_kernel"]),
             "per_kernel_ms": d["per_kernel"],
         }
     print(json.dumps(out), flush=True)
