@@ -9,7 +9,8 @@ HBM.  Prints ONE JSON line on stdout (details go to stderr):
              prefill, T=8192, H=7168, 256 routed experts + 1 shared, top-8)
   roofline   the dominant kernel (FC1 grouped GEMM): algorithmic bytes/FLOPs
              per launch / its mean launch duration from HIP events recorded on
-             the launch stream during the timed steps
+             the launch stream, over as many steps again as were timed (the
+             timed steps themselves run without the events)
   decode     the same figures for the DeepSeek-V3-shaped decode batch (T=512)
   cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
              workload on this host's cores (a reported baseline, not a target)
@@ -179,14 +180,19 @@ def run_workload(name, steps, warmup, device):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    moe.timing_enable(True)
-    moe.kernel_times(reset=True)
-    torch.cuda.synchronize()
+    # the timed steps run without per-launch events (they cost ~0.1 ms a step);
+    # the per-kernel breakdown comes from the same number of steps run after
+    # them with the library's HIP-event hooks on
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    moe.timing_enable(True)
+    moe.kernel_times(reset=True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     kt = moe.kernel_times(reset=True)
     moe.timing_enable(False)
     cnt = torch.bincount(layer.ids.flatten().long(), minlength=w.E).cpu()
