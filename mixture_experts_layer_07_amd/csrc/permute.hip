@@ -43,14 +43,19 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
                                                            int n_shared,
                                                            int32_t* __restrict__ offsets)
 {
+    constexpr int kBatch = 16;  // loads in flight per thread (the column walk is latency bound)
     __shared__ int tot[256];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = counts[(size_t)c * E + e];
-            counts[(size_t)c * E + e] = run;
-            run += v;
+        // pass 1: this expert's total over all chunks
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = (c0 + j < nchunks) ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) run += v[j];
         }
     }
     tot[e] = (e < E) ? run : 0;
@@ -65,7 +70,19 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
     const int base = (e < E) ? tot[e] - run : 0;
     if (e < E) {
         offsets[e] = base;
-        for (int c = 0; c < nchunks; ++c) counts[(size_t)c * E + e] += base;
+        // pass 2: each chunk's count becomes its first row for this expert
+        int acc = base;
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = (c0 + j < nchunks) ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (c0 + j < nchunks) counts[(size_t)(c0 + j) * E + e] = acc;
+                acc += v[j];
+            }
+        }
     }
     if (e == 0) {
         offsets[E] = P;
