@@ -274,6 +274,21 @@ def test_layer_parity_workloads(name):
     assert not torch.isnan(y).any()
 
 
+@pytest.mark.parametrize("wdt", ["bf16", "fp8"])
+def test_layer_several_shared_experts(wdt):
+    """Three shared experts (groups E, E+1, E+2: every token, weight 1) beside
+    top-3 routed experts, whole layer against the oracle on every token."""
+    w = small_workload("bf16", wdt, T=190, E=12, k=3, n_shared=3, method=1)
+    inp = wl.make_inputs(w, 7)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    layer, y = run_layer(w, g)
+    ids, sc, _ = oracle_route(w, inp["logits"], inp["bias"])
+    W = oracle.Weights(inp["w13"], inp["w2"], wdt, inp["w13_scale"], inp["w2_scale"])
+    toks = np.arange(w.T, dtype=np.int32)
+    ref = oracle.layer_tokens(W, inp["x"], "bf16", w.T, w.k, w.E, w.n_shared, ids, sc, toks)
+    assert rel_l2(host(y).double().numpy(), ref) < TOL[("bf16", wdt)]
+
+
 def test_layer_nan_poisoned_buffers_and_determinism():
     """Outputs and workspace pre-filled with NaN must not leak; two runs agree bitwise."""
     w = small_workload("bf16", "bf16", T=500, E=16, k=4, n_shared=1, method=2, n_group=4,
