@@ -38,12 +38,15 @@ def lib():
         L.oracle_decode_bf16.restype = C.c_double
         L.oracle_decode_e4m3.argtypes = [C.c_uint8]
         L.oracle_decode_e4m3.restype = C.c_double
+        L.oracle_encode_e4m3.argtypes = [C.c_float]
+        L.oracle_encode_e4m3.restype = C.c_uint8
+        L.oracle_quantize_fp8.argtypes = [P, i, i, i, P, P]
         L.oracle_sigmoid_f32.argtypes = [C.c_float, C.POINTER(C.c_int)]
         L.oracle_sigmoid_f32.restype = C.c_float
         L.oracle_route.argtypes = [P, i, i, i, i, i, i, P, C.c_double, i, P, P, P]
         L.oracle_permute.argtypes = [P, i, i, i, i, P, P, P]
-        L.oracle_expert_rows.argtypes = [C.POINTER(_Weights), P, i, i, i, i, i, P, P, P, i, P, P]
-        L.oracle_layer_tokens.argtypes = [C.POINTER(_Weights), P, i, i, i, i, i, P, P, P, i, P]
+        L.oracle_expert_rows.argtypes = [C.POINTER(_Weights), P, i, P, i, i, i, i, P, P, P, i, P, P]
+        L.oracle_layer_tokens.argtypes = [C.POINTER(_Weights), P, i, P, i, i, i, i, P, P, P, i, P]
         L.oracle_finalize.argtypes = [P, i, P, P, i, i, i, i, P]
         L.oracle_set_num_threads.argtypes = [i]
         _lib = L
@@ -89,6 +92,25 @@ def decode_bf16(bits: int) -> float:
 
 def decode_e4m3(bits: int) -> float:
     return lib().oracle_decode_e4m3(int(bits))
+
+
+def encode_e4m3(f: float) -> int:
+    """fp32 value -> OCP e4m3fn code (nearest, ties to even, saturating)."""
+    return int(lib().oracle_encode_e4m3(float(f)))
+
+
+def quantize_fp8(x, dt="bf16"):
+    """1x128 block quantisation of x [rows, cols] -> (codes uint8 [rows, cols],
+    scales float32 [rows, cols/128])."""
+    xa = _np(x)
+    rows, cols = xa.shape
+    q = np.zeros((rows, cols), np.uint8)
+    s = np.zeros((rows, cols // 128), np.float32)
+    rc = lib().oracle_quantize_fp8(_ptr(xa), DTYPE_CODE[dt] if isinstance(dt, str) else dt,
+                                   rows, cols, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize_fp8: cols must be a multiple of 128, dtype f32/bf16")
+    return q, s
 
 
 def sigmoid_f32(l: float):
@@ -143,32 +165,36 @@ class Weights:
 
 
 def expert_rows(W: Weights, x, act, T, k, E, n_shared, offsets, permuted_pair, rows,
-                want_h=False):
-    """FFN output rows (fp64 [len(rows), H]) and optionally h (fp64 [len(rows), I])."""
+                want_h=False, x_scale=None):
+    """FFN output rows (fp64 [len(rows), H]) and optionally h (fp64 [len(rows), I]).
+    act "fp8": x holds e4m3 codes with 1x128 scales x_scale [T, H/128]."""
     xa = _np(x)
+    xs = _np(x_scale, np.float32)
     off = _np(offsets, np.int32)
     pp = _np(permuted_pair, np.int32)
     rw = _np(rows, np.int32)
     out = np.zeros((len(rw), W.H), np.float64)
     h = np.zeros((len(rw), W.I), np.float64) if want_h else None
     rc = lib().oracle_expert_rows(C.byref(W.struct), _ptr(xa), DTYPE_CODE[act] if isinstance(act, str) else act,
-                                  T, k, E, n_shared, _ptr(off), _ptr(pp), _ptr(rw), len(rw),
+                                  _ptr(xs), T, k, E, n_shared, _ptr(off), _ptr(pp), _ptr(rw), len(rw),
                                   _ptr(h), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_expert_rows: row outside every group")
     return (out, h) if want_h else out
 
 
-def layer_tokens(W: Weights, x, act, T, k, E, n_shared, ids, scales, tokens):
-    """The layer output (fp64 [len(tokens), H]) by its definition."""
+def layer_tokens(W: Weights, x, act, T, k, E, n_shared, ids, scales, tokens, x_scale=None):
+    """The layer output (fp64 [len(tokens), H]) by its definition.
+    act "fp8": x holds e4m3 codes with 1x128 scales x_scale [T, H/128]."""
     xa = _np(x)
+    xs = _np(x_scale, np.float32)
     ia = _np(ids, np.int32)
     sa = _np(scales, np.float64)
     tk = _np(tokens, np.int32)
     y = np.zeros((len(tk), W.H), np.float64)
     rc = lib().oracle_layer_tokens(C.byref(W.struct), _ptr(xa),
                                    DTYPE_CODE[act] if isinstance(act, str) else act,
-                                   T, k, E, n_shared, _ptr(ia), _ptr(sa), _ptr(tk), len(tk),
+                                   _ptr(xs), T, k, E, n_shared, _ptr(ia), _ptr(sa), _ptr(tk), len(tk),
                                    _ptr(y))
     if rc != 0:
         raise ValueError("oracle_layer_tokens: token out of range")

@@ -22,6 +22,12 @@
  *  [GG]   "从 Dense GEMM 到 TP MoE 的演进逻辑" (gsyq.cn), sections 2.1-2.2
  *         (offset array marking each group's start; permute of each
  *         expert's tokens into one contiguous block).
+ *  fp8 activations: [TRT] sections "MoEScheduler:两条执行路径,两套相反的约定"
+ *         and "“自适应顺序”里的一个细节" (a quantise-input step of the backend
+ *         runs before the MoE GEMMs, before or after dispatch) and [VLLM]
+ *         section "量化与 MoE Kernel 选择" (the fp8 fused MoE follows
+ *         DeepSeek-V3's fp8 mixed-precision scheme; read here as 1x128
+ *         activation blocks and 128x128 weight blocks with fp32 scales).
  *
  * Readings of points the pages leave open (each also listed in the design
  * notes of the repository):
@@ -46,6 +52,13 @@
  *  - fp8 weights: OCP e4m3fn codes times an fp32 scale per 128x128 block of
  *    each [out, in] matrix.
  *  - The shared expert is group E (+s), weight 1.0, rows P + s*T + t.
+ *  - fp8 activations: each row is cut into blocks of 128 consecutive
+ *    channels; a block's scale is s = fl32(amax / 448) and its codes are
+ *    e4m3(fl32(v / s)), rounded to nearest, ties to even, saturating at
+ *    +-448; a block whose scale is 0 encodes as zeros.  The input x is
+ *    quantised once per token (before the permute); the FFN intermediate h
+ *    is rounded once to fp32 and quantised the same way per row and 128
+ *    intermediate channels before FC2.
  *
  * All floating point is fp64 except where the method itself fixes fp32 (the
  * selection keys).  Inputs in bf16/fp8/fp32 are decoded exactly to fp64.
@@ -98,6 +111,65 @@ static double load_elem(const void* base, int dtype, size_t i)
     default:
         return oracle_decode_e4m3(((const uint8_t*)base)[i]);
     }
+}
+
+/* fp32 -> OCP e4m3fn code: round to nearest, ties to even; magnitudes past
+ * the largest finite value (448) saturate to it; the sign of zero is kept;
+ * NaN -> 0x7F.  Normal codes hold (1 + m/8) 2^(e-7), subnormals m/8 2^-6, so
+ * the quantum is 2^-9 below 2^-6 and 2^(e-3) in binade [2^e, 2^(e+1)). */
+uint8_t oracle_encode_e4m3(float f)
+{
+    if (isnan(f))
+        return 0x7F;
+    uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* n/8 * 2^-6 for n = 0..8; n = 8 is the smallest normal, code 0x08 */
+        double n = rint(a / ldexp(1.0, -9)); /* exact scaling, ties to even */
+        return sign | (uint8_t)n;
+    }
+    int ex;
+    frexp(a, &ex); /* a = fr 2^ex, fr in [0.5, 1): binade e = ex - 1 */
+    int e = ex - 1;
+    double n = rint(a / ldexp(1.0, e - 3)); /* 8..16 */
+    if (n == 16.0) {
+        e += 1;
+        n = 8.0;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)n - 8));
+}
+
+/* One block of `n` fp32 values: s = fl32(amax / 448), q = e4m3(fl32(v / s)).
+ * Both divisions are single-precision IEEE divisions (correctly rounded). */
+static float quantize_block(const float* v, int n, uint8_t* q)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        if (fabsf(v[i]) > amax)
+            amax = fabsf(v[i]);
+    float s = amax / 448.0f;
+    for (int i = 0; i < n; ++i)
+        q[i] = (s == 0.0f) ? 0 : oracle_encode_e4m3(v[i] / s);
+    return s;
+}
+
+/* 1x128 block quantisation of x [rows, cols] (fp32 or bf16 values; cols a
+ * multiple of 128): q [rows, cols] e4m3 codes, s [rows, cols / 128]. */
+int oracle_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* q, float* s)
+{
+    if (cols % 128 != 0 || (dt != ORACLE_F32 && dt != ORACLE_BF16))
+        return -1;
+    float v[128];
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < cols / 128; ++b) {
+            size_t base = (size_t)r * cols + (size_t)b * 128;
+            for (int i = 0; i < 128; ++i)
+                v[i] = (float)load_elem(x, dt, base + i); /* exact */
+            s[(size_t)r * (cols / 128) + b] = quantize_block(v, 128, q + base);
+        }
+    return 0;
 }
 
 /* ---------------------------------------------------------------- routing */
@@ -325,9 +397,11 @@ static double weight_at(const void* w, int wdt, const float* scale, int g, int r
 
 /* Expert g applied to one activation row a[H]:
  *   gate = W1 a, up = W3 a (rows [0,I) and [I,2I) of w13[g]),
- *   h = silu(gate) * up, out = W2 h.  h_out (may be NULL) receives h. */
+ *   h = silu(gate) * up, out = W2 h.  h (size I) receives h.  With fp8
+ *   activations (quant_h), FC2 reads h rounded to fp32, quantised in 1x128
+ *   blocks and dequantised: hq = e4m3 value * block scale. */
 static void expert_apply(const oracle_weights* W, int g, const double* a, double* h,
-                         double* out)
+                         double* out, int quant_h)
 {
     int H = W->H, I = W->I;
     for (int i = 0; i < I; ++i) {
@@ -338,25 +412,47 @@ static void expert_apply(const oracle_weights* W, int g, const double* a, double
         }
         h[i] = gate / (1.0 + exp(-gate)) * up;
     }
+    const double* hin = h;
+    double* hq = NULL;
+    if (quant_h) {
+        hq = (double*)malloc(sizeof(double) * (size_t)I);
+        float v[128];
+        uint8_t q[128];
+        for (int b = 0; b < I / 128; ++b) {
+            for (int i = 0; i < 128; ++i)
+                v[i] = (float)h[b * 128 + i];
+            float s = quantize_block(v, 128, q);
+            for (int i = 0; i < 128; ++i)
+                hq[b * 128 + i] = oracle_decode_e4m3(q[i]) * (double)s;
+        }
+        hin = hq;
+    }
     for (int o = 0; o < H; ++o) {
         double acc = 0.0;
         for (int i = 0; i < I; ++i)
-            acc += weight_at(W->w2, W->wdt, W->w2_scale, g, H, I, o, i) * h[i];
+            acc += weight_at(W->w2, W->wdt, W->w2_scale, g, H, I, o, i) * hin[i];
         out[o] = acc;
     }
+    free(hq);
 }
 
-static void load_row(const void* x, int act, int H, int t, double* a)
+/* Activation row t, exact in fp64; fp8 codes are dequantised with their
+ * row's 1x128 block scales x_scale [T, H/128]. */
+static void load_row(const void* x, int act, const float* x_scale, int H, int t, double* a)
 {
-    for (int c = 0; c < H; ++c)
+    for (int c = 0; c < H; ++c) {
         a[c] = load_elem(x, act, (size_t)t * H + c);
+        if (act == ORACLE_FP8)
+            a[c] *= (double)x_scale[(size_t)t * (H / 128) + c / 128];
+    }
 }
 
 /* Output rows of the expert FFN for the permuted rows listed in `rows`:
  * row r belongs to the group g with offsets[g] <= r < offsets[g+1]; its token
  * is permuted_pair[r] / k for routed groups and r - offsets[g] for shared
  * ones.  out: [n_rows, H];  h_out (nullable): [n_rows, I]. */
-int oracle_expert_rows(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+int oracle_expert_rows(const oracle_weights* W, const void* x, int act, const float* x_scale,
+                       int T, int k, int E,
                        int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
                        const int32_t* rows, int n_rows, double* h_out, double* out)
 {
@@ -375,8 +471,8 @@ int oracle_expert_rows(const oracle_weights* W, const void* x, int act, int T, i
         int t = (g < E) ? permuted_pair[r] / k : r - offsets[g];
         double* a = (double*)malloc(sizeof(double) * (size_t)W->H);
         double* h = (double*)malloc(sizeof(double) * (size_t)W->I);
-        load_row(x, act, W->H, t, a);
-        expert_apply(W, g, a, h, out + (size_t)i * W->H);
+        load_row(x, act, x_scale, W->H, t, a);
+        expert_apply(W, g, a, h, out + (size_t)i * W->H, act == ORACLE_FP8);
         if (h_out)
             memcpy(h_out + (size_t)i * W->I, h, sizeof(double) * (size_t)W->I);
         free(a);
@@ -389,7 +485,8 @@ int oracle_expert_rows(const oracle_weights* W, const void* x, int act, int T, i
 /* The layer by its definition, for the tokens listed in `tokens`:
  *   y_t = sum_j scales[t,j] * E_{ids[t,j]}(x_t)  +  sum_s E_{E+s}(x_t).
  * No permute is involved.  y: [n_tokens, H]. */
-int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, const float* x_scale,
+                        int T, int k, int E,
                         int n_shared, const int32_t* ids, const double* scales,
                         const int32_t* tokens, int n_tokens, double* y)
 {
@@ -406,16 +503,16 @@ int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, int T, 
         double* h = (double*)malloc(sizeof(double) * (size_t)W->I);
         double* o = (double*)malloc(sizeof(double) * (size_t)H);
         double* yt = y + (size_t)i * H;
-        load_row(x, act, H, t, a);
+        load_row(x, act, x_scale, H, t, a);
         for (int c = 0; c < H; ++c)
             yt[c] = 0.0;
         for (int j = 0; j < k; ++j) {
-            expert_apply(W, ids[(size_t)t * k + j], a, h, o);
+            expert_apply(W, ids[(size_t)t * k + j], a, h, o, act == ORACLE_FP8);
             for (int c = 0; c < H; ++c)
                 yt[c] += scales[(size_t)t * k + j] * o[c];
         }
         for (int s = 0; s < n_shared; ++s) {
-            expert_apply(W, E + s, a, h, o);
+            expert_apply(W, E + s, a, h, o, act == ORACLE_FP8);
             for (int c = 0; c < H; ++c)
                 yt[c] += o[c];
         }

@@ -31,6 +31,8 @@ typedef struct {
 
 double oracle_decode_bf16(uint16_t bits);
 double oracle_decode_e4m3(uint8_t bits);
+uint8_t oracle_encode_e4m3(float f);
+int oracle_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* q, float* s);
 float oracle_sigmoid_f32(float l, int* hard);
 
 int oracle_route(const float* logits, int T, int E, int method, int k, int n_group,
@@ -38,10 +40,14 @@ int oracle_route(const float* logits, int T, int E, int method, int k, int n_gro
                  int32_t* ids, double* scales, int64_t* hard_cases);
 int oracle_permute(const int32_t* ids, int T, int k, int E, int n_shared, int32_t* offsets,
                    int32_t* permuted_pair, int32_t* unpermute);
-int oracle_expert_rows(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+/* act == ORACLE_FP8: x holds e4m3 codes [T, H] with 1x128 scales x_scale [T, H/128]
+ * (NULL otherwise), and h is quantised the same way before FC2. */
+int oracle_expert_rows(const oracle_weights* W, const void* x, int act, const float* x_scale,
+                       int T, int k, int E,
                        int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
                        const int32_t* rows, int n_rows, double* h_out, double* out);
-int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, int T, int k, int E,
+int oracle_layer_tokens(const oracle_weights* W, const void* x, int act, const float* x_scale,
+                        int T, int k, int E,
                         int n_shared, const int32_t* ids, const double* scales,
                         const int32_t* tokens, int n_tokens, double* y);
 int oracle_finalize(const void* fc2, int dt, const int32_t* unpermute, const double* scales,
