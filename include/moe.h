@@ -12,6 +12,9 @@
  *   moe_expert_ffn grouped GEMM FC1 with fused SwiGLU, then grouped GEMM FC2
  *   moe_finalize   weighted gather-sum of each token's k FFN rows (+ shared)
  *
+ * With fp8 activations the FFN step is moe_quantize_fp8 (of x) followed by
+ * moe_expert_ffn_fp8; route, permute and finalize are unchanged.
+ *
  * Conventions shared by every call:
  *  - Pointers named as device buffers are device pointers (hipMalloc'd or
  *    torch CUDA tensors); scalars are passed by value.  All arrays are dense,
@@ -183,8 +186,58 @@ moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
                         const float* scales, int T, int k, int H, int n_shared, void* y,
                         int ydt, void* stream);
 
+/*
+ * moe_quantize_fp8 -- the quantise-input step that precedes the MoE GEMMs
+ * (TensorRT-LLM page, sections "MoEScheduler:两条执行路径,两套相反的约定" and
+ * "“自适应顺序”里的一个细节"), in the form of the fp8 fused MoE on the vLLM page
+ * (section "量化与 MoE Kernel 选择", after DeepSeek-V3's fp8 scheme): every row
+ * is cut into blocks of 128 consecutive values;
+ *     s = fl32(amax / 448),   code = e4m3fn(fl32(v / s))
+ * rounded to nearest even and saturating at +-448 (OCP e4m3fn codes); a block
+ * whose scale is 0 encodes as zeros.  Call it on x [T, H] once per layer,
+ * before the permute (one GPU has no dispatch, and quantising the T tokens
+ * writes k times fewer bytes than quantising the T*k permuted rows).
+ *
+ *  x        device [rows, cols] in `dt` (MOE_BF16 or MOE_F32).
+ *  cols     a multiple of 128.
+ *  xq       device uint8 [rows, cols] out: e4m3fn codes.
+ *  x_scale  device fp32 [rows, cols / 128] out.
+ * Codes and scales are deterministic and bit-exact.  NaN inputs give
+ * unspecified codes.
+ */
+moe_status moe_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* xq,
+                            float* x_scale, void* stream);
+
+/*
+ * moe_expert_ffn_fp8 -- moe_expert_ffn with fp8 activations on fp8 x fp8 MFMA
+ * (vLLM page, section "量化与 MoE Kernel 选择"):
+ *     h_r   = silu(W1_g xq_t) * (W3_g xq_t),  xq_t = dequantised x_t
+ *     hq_r  = h_r rounded to fp32, quantised like moe_quantize_fp8 per row and
+ *             128 intermediate channels
+ *     out_r = W2_g hq_r
+ * Products of e4m3 codes are exact; sums are fp32; each 128-wide K block is
+ * added times (activation block scale x weight block scale).
+ *
+ *  xq, x_scale   moe_quantize_fp8 of x [T, H].
+ *  w13, w2, w13_scale, w2_scale   fp8 e4m3fn weights with fp32 128x128 block
+ *             scales, laid out as for moe_expert_ffn with wdt MOE_FP8_E4M3.
+ *  fc2_out    device bf16 [T*k + n_shared*T, H] out (unweighted FFN rows).
+ *  ws         device workspace of moe_workspace_size(T, k, E, n_shared, H, I,
+ *             MOE_FP8_E4M3) bytes.  On return it holds hq: e4m3fn codes
+ *             [R, I] at byte 0 (R = T*k + n_shared*T, rows in permuted order)
+ *             and their fp32 scales [R, I/128] from the next 256-byte
+ *             boundary.
+ * H and I are multiples of 128; other arguments as for moe_expert_ffn.
+ */
+moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H, int I, int k,
+                              int E, int n_shared, const int32_t* expert_offsets,
+                              const int32_t* permuted_pair, const uint8_t* w13, const uint8_t* w2,
+                              const float* w13_scale, const float* w2_scale, void* fc2_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace that moe_permute and moe_expert_ffn need for this shape
- * (0 on invalid arguments).  One buffer of this size serves both calls. */
+ * (0 on invalid arguments).  One buffer of this size serves both calls.
+ * act = MOE_FP8_E4M3 sizes it for moe_expert_ffn_fp8. */
 size_t moe_workspace_size(int T, int k, int E, int n_shared, int H, int I, int act);
 
 /* Static description of a status code. */
@@ -207,7 +260,8 @@ enum {
     MOE_KID_FC1 = 4,
     MOE_KID_FC2 = 5,
     MOE_KID_FINALIZE = 6,
-    MOE_NUM_KIDS = 7
+    MOE_KID_QUANT = 7,
+    MOE_NUM_KIDS = 8
 };
 moe_status moe_timing_enable(int enable);
 moe_status moe_kernel_times(double* ms /*[MOE_NUM_KIDS]*/, int64_t* launches /*[MOE_NUM_KIDS]*/,

@@ -141,9 +141,11 @@ const char* moe_last_error(void) { return g_err; }
 size_t moe_workspace_size(int T, int k, int E, int n_shared, int H, int I, int act)
 {
     (void)H;
-    if (check_common(T, k, E, n_shared) != MOE_OK || I < 0 || !valid_act(act)) return 0;
+    if (check_common(T, k, E, n_shared) != MOE_OK || I < 0 || !(valid_act(act) || act == MOE_FP8_E4M3))
+        return 0;
     const size_t a = align256(permute_scratch_bytes(T, k, E));
-    const size_t b = ffn_scratch_bytes(T, k, n_shared, I, act);
+    const size_t b = act == MOE_FP8_E4M3 ? ffn_fp8_scratch_bytes(T, k, n_shared, I)
+                                         : ffn_scratch_bytes(T, k, n_shared, I, act);
     return (a > b ? a : b) + 256;
 }
 
@@ -227,6 +229,42 @@ moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, in
                       wdt == MOE_FP8_E4M3 ? w13_scale : nullptr,
                       wdt == MOE_FP8_E4M3 ? w2_scale : nullptr, fc2_out, ws,
                       static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* xq,
+                            float* x_scale, void* stream)
+{
+    if (rows < 0) return set_error(MOE_ERR_INVALID_ARG, "rows must be >= 0 (got %d)", rows);
+    if (cols < 1) return set_error(MOE_ERR_INVALID_ARG, "cols must be positive (got %d)", cols);
+    if (cols % 128) return set_error(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 128 (got %d)", cols);
+    if (!valid_act(dt)) return set_error(MOE_ERR_INVALID_ARG, "x dtype %d must be MOE_F32 or MOE_BF16", dt);
+    if (rows == 0) return MOE_OK;
+    if (!x || !xq || !x_scale) return set_error(MOE_ERR_INVALID_ARG, "x, xq and x_scale must be non-null");
+    return launch_quantize_fp8(x, dt, rows, cols, xq, x_scale, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H, int I, int k,
+                              int E, int n_shared, const int32_t* expert_offsets,
+                              const int32_t* permuted_pair, const uint8_t* w13, const uint8_t* w2,
+                              const float* w13_scale, const float* w2_scale, void* fc2_out,
+                              void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_common(T, k, E, n_shared);
+    if (st != MOE_OK) return st;
+    if (H < 1 || I < 1) return set_error(MOE_ERR_INVALID_ARG, "H and I must be positive (H=%d, I=%d)", H, I);
+    if (H % 128 || I % 128)
+        return set_error(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (H=%d, I=%d)", H, I);
+    if (T == 0) return MOE_OK;
+    if (!xq || !x_scale || !expert_offsets || !w13 || !w2 || !w13_scale || !w2_scale || !fc2_out ||
+        (E > 0 && !permuted_pair))
+        return set_error(MOE_ERR_INVALID_ARG,
+                         "xq, x_scale, expert_offsets, permuted_pair, w13, w2, their scales and fc2_out "
+                         "must be non-null");
+    const size_t need = ffn_fp8_scratch_bytes(T, k, n_shared, I);
+    if (!ws || ws_bytes < need)
+        return set_error(MOE_ERR_WORKSPACE, "expert_ffn_fp8 needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    return launch_ffn_fp8(xq, x_scale, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2,
+                          w13_scale, w2_scale, fc2_out, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,

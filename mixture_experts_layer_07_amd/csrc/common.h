@@ -70,6 +70,21 @@ __device__ __forceinline__ void store8_f32(float* p, const float v[8])
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Four fp32 values -> four OCP e4m3fn codes of v / s (one IEEE division
+// each), round to nearest even, packed little-endian; s == 0 gives zeros.
+// The conversion instruction turns magnitudes above 464 into NaN, so the
+// quotient is clamped to +-448 first, which is exactly saturation (448 is the
+// largest finite value and everything in [448, 464) rounds to it anyway).
+__device__ __forceinline__ uint32_t fp8x4_code(const float (&v)[4], float s)
+{
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (s == 0.0f) ? 0.0f : fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+    return (uint32_t)w;
+}
+
 // ------------------------------------------------------------ host side
 struct TimedLaunch {
     TimedLaunch(int kid, hipStream_t s);
@@ -96,6 +111,13 @@ moe_status launch_ffn(const void* x, int act, int T, int H, int I, int k, int E,
                       const int32_t* offsets, const int32_t* permuted_pair, const void* w13,
                       const void* w2, int wdt, const float* w13_scale, const float* w2_scale,
                       void* fc2_out, void* ws, hipStream_t s);
+size_t ffn_fp8_scratch_bytes(int T, int k, int n_shared, int I);
+moe_status launch_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H, int I, int k, int E,
+                          int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
+                          const uint8_t* w13, const uint8_t* w2, const float* w13_scale,
+                          const float* w2_scale, void* fc2_out, void* ws, hipStream_t s);
+moe_status launch_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t s);
 moe_status launch_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
                            const float* scales, int T, int k, int H, int n_shared, void* y,
                            int ydt, hipStream_t s);

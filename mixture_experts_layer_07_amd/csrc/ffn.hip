@@ -27,9 +27,10 @@
 //          16-byte fragment (lane group q feeds K = 4q + i to the i-th MFMA,
 //          the same for A and B, so the four products cover the 16 K values
 //          once).
-//   Direct-to-LDS engine (bf16 activations, bf16 or fp8 weights): described
-//          at DmaCfg below; v_mfma_f32_16x16x32_bf16, a lane feeding 8
-//          consecutive K values of one row of A and of B.
+//   Direct-to-LDS engine (bf16 activations with bf16 or fp8 weights, or
+//          fp8 activations with fp8 weights): described at DmaCfg below;
+//          v_mfma_f32_16x16x32_bf16, a lane feeding 8 consecutive K values
+//          of one row of A and of B, or v_mfma_f32_16x16x128_f8f6f4 with 32.
 // FC1 keeps the gate and up halves of an output column in the same lane: the
 // staged B tile alternates 16 gate rows and the matching 16 up rows, so MFMA
 // column blocks 2q and 2q+1 are gate and up of the same 16 outputs and the
@@ -49,6 +50,8 @@ struct FfnArgs {
     const char* a_src;         // FC1: x [T, H];  FC2: h [R, I]
     const char* w;             // FC1: w13 [G, 2I, H];  FC2: w2 [G, H, I]
     const float* wscale;       // fp8 block scales or null
+    const float* ascale;       // fp8 activations: FC1 x scales [T, H/128], FC2 h scales [R, I/128]
+    float* out_scale;          // fp8 activations, FC1: h scales [R, I/128] out
     char* out;                 // FC1: h [R, I];  FC2: fc2_out [R, H]
     const int32_t* offsets;    // [G + 1]
     const int32_t* permuted_pair;
@@ -426,26 +429,43 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 // sums of one 128-wide K block go into a partial tile that is added to the
 // accumulator times the block's fp32 scale (exact in the scale), so the only
 // rounding besides fp32 accumulation is the one of the output.
-template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool W8_ = false>
+//
+// fp8 activations (A8, with fp8 weights): a stage is one 128-wide K block,
+// 128-byte rows of fp8 codes for both operands, multiplied on
+// v_mfma_f32_16x16x128_f8f6f4 (exact products, fp32 sums).  Each wave also
+// stages the 1x128 activation scales of its own WTM rows for that block (one
+// 4-byte-per-lane transfer into a private 256-byte slot), and adds each
+// block's MFMA result to the accumulator times (row scale x weight-block
+// scale).  FC1's epilogue quantises h per row and 128 intermediate channels
+// (one 256-column tile holds exactly one such block of every row).
+template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool W8_ = false, bool A8_ = false>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
-    static constexpr bool W8 = W8_;
+    static constexpr bool A8 = A8_;
+    static constexpr bool W8 = W8_ || A8_;                 // fp8 weights
+    static constexpr bool WNARROW = W8 && !A8;             // fp8 weights widened to bf16
     static constexpr int NT = WM * WN * 64;
     static constexpr int NW = WM * WN;
-    static constexpr int BK = 64;                          // K per stage
-    static constexpr int KSTEPS = BK / 32;                 // MFMA K-steps per stage
-    static constexpr int BROWB = W8 ? 64 : 128;            // weight bytes per staged row
+    static constexpr int BK = A8 ? 128 : 64;               // K per stage
+    static constexpr int KSTEPS = A8 ? 1 : BK / 32;        // MFMA K-steps per stage
+    static constexpr int BROWB = WNARROW ? 64 : 128;       // weight bytes per staged row
     static constexpr int A_OPS = BM / 8;                   // 1 KB DMA ops per stage, activations
     static constexpr int B_OPS = BN * BROWB / 1024;        // ... and weights
     static constexpr int A_BYTES = BM * 128;
-    static constexpr int STAGE = A_BYTES + BN * BROWB;     // bytes per stage
+    static constexpr int B_BYTES = BN * BROWB;
+    static constexpr int SA_BYTES = A8 ? NW * 256 : 0;     // per-wave activation-scale slots
+    static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;  // bytes per stage
     static constexpr int NINS = A_OPS + B_OPS;
-    static constexpr int IPW = NINS / NW;                  // ops per wave per stage
+    static constexpr int IPW_AB = NINS / NW;               // 1 KB ops per wave per stage
+    static constexpr int IPW = IPW_AB + (A8 ? 1 : 0);      // ... plus the scale transfer
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static_assert(BM % 8 == 0 && NINS % NW == 0 && IPW >= 1, "DMA ops split evenly over waves");
+    static constexpr int AMAX_BYTES = A8 ? BM * WN * 4 : 4;  // FC1 epilogue: row maxima per wave column
+    static_assert(BM % 8 == 0 && NINS % NW == 0 && IPW_AB >= 1, "DMA ops split evenly over waves");
     static_assert(WTM % 16 == 0 && WTN % 32 == 0, "tile");
-    static_assert(S >= 2 && S <= 8 && S * STAGE <= 152 * 1024, "ring (LDS also holds the tile tables)");
+    static_assert(!A8 || (WTM <= 64 && BN == 256), "A8: one scale transfer per wave; 128 h columns per tile");
+    static_assert(S >= 2 && S <= 8 && S * STAGE + AMAX_BYTES <= 156 * 1024,
+                  "ring (LDS also holds the tile tables)");
 };
 
 // Byte offset of logical 16-byte chunk kc of a staged 128-byte row: chunk
@@ -503,6 +523,33 @@ __device__ __forceinline__ void dma16(unsigned lds_addr, const char* src)
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");
 }
 
+// Same with 4 bytes per lane: lane l lands at byte 4*l of the 256 bytes at
+// `lds_addr`.
+__device__ __forceinline__ void dma4(unsigned lds_addr, const char* src)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// 16x16x128 MFMA on e4m3 codes (format 0 for both operands); its per-lane
+// power-of-two block-scale operands are left at 2^0 (E8M0 code 127).
+__device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                            127, 0, 127);
+}
+
+// 32 fp8 codes of one row at K bytes [32 g, 32 g + 32) of a staged 128-byte
+// row: logical chunks 2g and 2g+1.
+__device__ __forceinline__ i32x8_t lds_row32(const char* base, int row, int g)
+{
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, 2 * g));
+    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, 2 * g + 1));
+    return i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
 // Barrier that orders LDS only (s_waitcnt lgkmcnt(0) + s_barrier): unlike
 // __syncthreads() it does not wait for the DMA loads still in flight.
 __device__ __forceinline__ void lds_barrier()
@@ -518,6 +565,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     __shared__ __attribute__((aligned(1024))) char lds[C::S * C::STAGE];
     __shared__ int s_off[kMaxGroups + 1];
     __shared__ int s_tile0[kMaxGroups + 1];
+    __shared__ float s_amax[C::AMAX_BYTES / 4];  // A8 FC1 epilogue: [BM][WN] row maxima
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -560,38 +608,53 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     if (tile >= total) return;
 
     const int nk = a.K / C::BK;
-    const size_t a_ld = (size_t)a.K * 2, w_ld = (size_t)a.K * (C::W8 ? 1 : 2);
+    const size_t a_ld = (size_t)a.K * (C::A8 ? 1 : 2), w_ld = (size_t)a.K * (C::W8 ? 1 : 2);
     const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds;
 
-    // Op o = q*NW + wave of a stage (wave-uniform) stages activation rows
-    // 8o .. 8o+7 when o < A_OPS, else weight rows: 8 bf16 or 16 fp8 rows from
-    // row (o - A_OPS) * rows-per-op.  Lane l writes the op's LDS bytes
-    // [16l, 16l+16): row l / 8 (l / 4 for fp8 rows) of the op, physical chunk
-    // l % 8 (l % 4), which holds logical chunk physical ^ swizzle(row).
-    auto op_is_a = [&](int q) { return q * C::NW + wave < C::A_OPS; };
-    auto op_row = [&](int q) {  // A row, or B row, of this lane in op q
+    // Op o = q*NW + wave of a stage (wave-uniform, q < IPW_AB) stages
+    // activation rows 8o .. 8o+7 when o < A_OPS, else weight rows: 8 rows of
+    // 128 bytes or 16 narrow fp8 rows of 64 bytes from row (o - A_OPS) *
+    // rows-per-op.  Lane l writes the op's LDS bytes [16l, 16l+16): row l / 8
+    // (l / 4 for narrow rows) of the op, physical chunk l % 8 (l % 4), which
+    // holds logical chunk physical ^ swizzle(row).  With fp8 activations op
+    // q = IPW_AB of every wave stages the activation scales of the wave's own
+    // rows: lane l fetches the scale of row wm*WTM + l % WTM.
+    auto op_is_s = [&](int q) { return C::A8 && q == C::IPW_AB; };
+    auto op_is_a = [&](int q) { return q < C::IPW_AB && q * C::NW + wave < C::A_OPS; };
+    auto op_row = [&](int q) {  // A row, or B row, of this lane in op q < IPW_AB
         const int o = q * C::NW + wave;
         if (o < C::A_OPS) return o * 8 + (lane >> 3);
-        return C::W8 ? (o - C::A_OPS) * 16 + (lane >> 2) : (o - C::A_OPS) * 8 + (lane >> 3);
+        return C::WNARROW ? (o - C::A_OPS) * 16 + (lane >> 2) : (o - C::A_OPS) * 8 + (lane >> 3);
     };
     auto op_chunk = [&](int q, int row) {  // logical 16-byte chunk this lane fetches
-        if (op_is_a(q) || !C::W8) return (lane & 7) ^ (row & 7);
+        if (op_is_a(q) || !C::WNARROW) return (lane & 7) ^ (row & 7);
         return (lane & 3) ^ ((row >> 2) & 3);
     };
+    const int s_row = wm * C::WTM + lane % C::WTM;  // scale op: this lane's tile row
 
     // For FC1 A rows the token comes from permuted_pair: a_raw() only loads the
     // entry (from an always-valid address) and source() interprets it, so the
     // next tile's loads can be issued early and consumed a whole tile later.
     auto a_raw = [&](const TileInfo& ti, int q) -> int {
-        const int row = op_row(q);
-        if (MODE == FC2 || !op_is_a(q)) return 0;
-        const int rr = ti.m0 + row;
+        if (MODE == FC2 || !(op_is_a(q) || op_is_s(q))) return 0;
+        const int rr = ti.m0 + (op_is_s(q) ? s_row : op_row(q));
         const int i = (ti.g < a.E && rr < ti.nrows) ? ti.row0 + rr : 0;
         // global-space load: a flat load would also count in lgkmcnt and make
         // the LDS-only barriers wait for it
         return *(const __attribute__((address_space(1))) int*)(a.permuted_pair + i);
     };
     auto source = [&](const TileInfo& ti, int q, int raw) -> const char* {
+        if (op_is_s(q)) {
+            const int rr = ti.m0 + s_row;
+            long r;
+            if (MODE == FC1) {
+                const int tok = (rr >= ti.nrows) ? 0 : (ti.g < a.E ? raw / a.k : rr);
+                r = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            } else {
+                r = ti.row0 + (rr < ti.nrows ? rr : 0);
+            }
+            return reinterpret_cast<const char*>(a.ascale + (size_t)r * (a.K / 128));
+        }
         const int row = op_row(q);
         const char* p;
         if (op_is_a(q)) {
@@ -621,9 +684,12 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     const char* src[C::IPW];
     auto issue = [&](int st, int kt) {
 #pragma unroll
-        for (int q = 0; q < C::IPW; ++q)
+        for (int q = 0; q < C::IPW_AB; ++q)
             dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + (q * C::NW + wave) * 1024),
                   src[q] + (size_t)kt * (op_is_a(q) ? 128 : C::BROWB));
+        if constexpr (C::A8)
+            dma4(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + C::A_BYTES + C::B_BYTES + wave * 256),
+                 src[C::IPW_AB] + (size_t)kt * 4);
     };
     // this wave's transfers of a slice have landed while `later` newer slices'
     // transfers (IPW each) may still be in flight
@@ -654,12 +720,12 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         }
 
         f32x4_t acc[C::MI][C::NI];
-        f32x4_t part[C::W8 ? C::MI : 1][C::W8 ? C::NI : 1];  // fp8: this K block's sums
+        f32x4_t part[C::WNARROW ? C::MI : 1][C::WNARROW ? C::NI : 1];  // fp8: this K block's sums
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if constexpr (C::W8) {
+        if constexpr (C::WNARROW) {
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -672,6 +738,38 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             if (kt + C::S - 1 < nk) issue((ring + kt + C::S - 1) % C::S, kt + C::S - 1);
             const char* la = lds + ((ring + kt) % C::S) * C::STAGE;
             const char* lb = la + C::A_BYTES;
+            if constexpr (C::A8) {
+                // one 128-wide K block: acc += (row scale x weight-block scale) * A.B
+                const int sk = a.K / 128;
+                const __attribute__((address_space(4))) float* wsp =
+                    (const __attribute__((address_space(4))) float*)a.wscale;
+                float sw0, sw1;  // weight-block scales of this wave's columns (FC1: gate, up)
+                if (MODE == FC1) {
+                    const int col = cur.nt * (C::BN / 2);  // the tile's 128 h columns
+                    sw0 = wsp[((size_t)cur.g * (a.N / 128) + col / 128) * sk + kt];
+                    sw1 = wsp[((size_t)cur.g * (a.N / 128) + (a.I + col) / 128) * sk + kt];
+                } else {
+                    const int wrow = min(cur.nt * C::BN + wn * C::WTN, a.N - 1);
+                    sw0 = sw1 = wsp[((size_t)cur.g * (a.N / 128) + wrow / 128) * sk + kt];
+                }
+                const float* lsa = reinterpret_cast<const float*>(lb + C::B_BYTES + wave * 256);
+                const int g4 = lane >> 4;
+                f32x4_t sa[C::MI];
+                i32x8_t fa[C::MI];
+#pragma unroll
+                for (int mi = 0; mi < C::MI; ++mi) {
+                    sa[mi] = *reinterpret_cast<const f32x4_t*>(lsa + mi * 16 + g4 * 4);
+                    fa[mi] = lds_row32(la, wm * C::WTM + mi * 16 + (lane & 15), g4);
+                }
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni) {
+                    const i32x8_t fb = lds_row32(lb, wn * C::WTN + ni * 16 + (lane & 15), g4);
+                    const float sw = (ni & 1) ? sw1 : sw0;
+#pragma unroll
+                    for (int mi = 0; mi < C::MI; ++mi)
+                        acc[mi][ni] += sa[mi] * (sw * mfma_fp8(fa[mi], fb));
+                }
+            } else {
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
                 const int kc = ks * 4 + (lane >> 4);
@@ -682,7 +780,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
                     const int row = wn * C::WTN + ni * 16 + (lane & 15);
-                    if constexpr (C::W8) {
+                    if constexpr (C::WNARROW) {
                         // 8 fp8 values at K = 32*ks + 8*(lane/16): byte 8*(4*ks + lane/16)
                         // of the 64-byte row, in 16-byte chunk 2*ks + lane/32
                         typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
@@ -697,11 +795,12 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < C::NI; ++ni) {
-                        if constexpr (C::W8) part[mi][ni] = mfma_frag(fa[mi], fb[ni], part[mi][ni], bf16_t());
+                        if constexpr (C::WNARROW) part[mi][ni] = mfma_frag(fa[mi], fb[ni], part[mi][ni], bf16_t());
                         else acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
                     }
             }
-            if constexpr (C::W8) {
+            }
+            if constexpr (C::WNARROW) {
                 if (kt & 1) {
                     // end of a 128-wide K block: acc += block scale * partial.  The
                     // scale index is wave-uniform; the constant address space makes
@@ -749,7 +848,56 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
         const int erow = (lane >> 4) * 4 + (lane & 3);  // row within a 16x16 block
         const int ecol = lane & 12;                      // first of its 4 columns
-        if (MODE == FC1) {
+        if (MODE == FC1 && C::A8) {
+            // h -> e4m3 per row and 128 intermediate channels: the tile's 128 h
+            // columns are split over the WN wave columns, 4 lanes per row each.
+            // h (quad-transposed) overwrites the gate accumulators.
+            float rmax[C::MI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi) {
+                rmax[mi] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < C::NI / 2; ++q) {
+                    float hv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float gt = acc[mi][2 * q][i];
+                        const float up = acc[mi][2 * q + 1][i];
+                        hv[i] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
+                    }
+                    quad_transpose(hv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[mi][2 * q][i] = hv[i];
+                        rmax[mi] = fmaxf(rmax[mi], fabsf(hv[i]));
+                    }
+                }
+                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 4, 64));
+                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 8, 64));
+                if (((lane >> 2) & 3) == 0) s_amax[(wm * C::WTM + mi * 16 + erow) * C::WN + wn] = rmax[mi];
+            }
+            lds_barrier();
+            uint8_t* hq = reinterpret_cast<uint8_t*>(a.out);
+            const int sk_out = a.I / 128;
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int w = 0; w < C::WN; ++w) amax = fmaxf(amax, s_amax[(wm * C::WTM + mi * 16 + erow) * C::WN + w]);
+                const float sc = amax / 448.0f;
+                const int rr = cur.m0 + wm * C::WTM + mi * 16 + erow;
+                if (rr < cur.nrows) {
+                    const size_t r = (size_t)(cur.row0 + rr);
+#pragma unroll
+                    for (int q = 0; q < C::NI / 2; ++q) {
+                        const float hv[4] = {acc[mi][2 * q][0], acc[mi][2 * q][1], acc[mi][2 * q][2], acc[mi][2 * q][3]};
+                        const int col = cur.nt * (C::BN / 2) + ((wn * C::WTN) / 32 + q) * 16 + ecol;
+                        *(__attribute__((address_space(1))) uint32_t*)(hq + r * a.I + col) = fp8x4_code(hv, sc);
+                    }
+                    if (wn == 0 && ((lane >> 2) & 3) == 0) a.out_scale[r * sk_out + cur.nt] = sc;
+                }
+            }
+        } else if (MODE == FC1) {
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -898,6 +1046,17 @@ moe_status run_ffn<bf16_t, fp8_t>(const FfnArgs& fc1, const FfnArgs& fc2, int R,
     return run_classes_w8<FC2>(fc2, R, s, MOE_KID_FC2);
 }
 
+// fp8 activations and weights: every class on fp8 MFMA, 256-column tiles (one
+// 128-channel block of h per FC1 tile).  Big groups: 8 waves of 64x128
+// (16 waves of 64x64 would not fit their operands and accumulators in 128
+// VGPRs); mid: 8 waves of 64x64; skinny: 32x256 with a 4-deep ring.
+template <int MODE>
+moe_status run_classes_a8(const FfnArgs& f, int R, hipStream_t s, int kid)
+{
+    return run_classes_dma<MODE, DmaCfg<32, 256, 1, 4, 2, 4, true, true>, DmaCfg<128, 256, 2, 4, 2, 3, true, true>,
+                           DmaCfg<256, 256, 4, 2, 4, 2, true, true>>(f, R, s, kid);
+}
+
 // fp32 (small reference-precision layers): one 32x128 tile shape for all groups.
 template <>
 moe_status run_ffn<float, float>(const FfnArgs& fc1, const FfnArgs& fc2, int R, hipStream_t s)
@@ -911,6 +1070,45 @@ moe_status run_ffn<float, float>(const FfnArgs& fc1, const FfnArgs& fc2, int R, 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
+
+size_t ffn_fp8_scratch_bytes(int T, int k, int n_shared, int I)
+{
+    const size_t R = (size_t)T * k + (size_t)n_shared * T;
+    return align256(R * (size_t)I) + align256(R * (size_t)(I / 128) * 4);
+}
+
+moe_status launch_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H, int I, int k, int E,
+                          int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
+                          const uint8_t* w13, const uint8_t* w2, const float* w13_scale,
+                          const float* w2_scale, void* fc2_out, void* ws, hipStream_t s)
+{
+    const int G = E + n_shared;
+    const int R = T * k + n_shared * T;
+    char* hq = static_cast<char*>(ws);
+    float* hs = reinterpret_cast<float*>(hq + align256((size_t)R * I));
+    FfnArgs f1{};
+    f1.a_src = reinterpret_cast<const char*>(xq);
+    f1.ascale = x_scale;
+    f1.w = reinterpret_cast<const char*>(w13);
+    f1.wscale = w13_scale;
+    f1.out = hq;
+    f1.out_scale = hs;
+    f1.offsets = offsets;
+    f1.permuted_pair = permuted_pair;
+    f1.T = T; f1.k = k; f1.E = E; f1.G = G; f1.I = I;
+    f1.N = 2 * I; f1.K = H; f1.out_ld = I;
+    FfnArgs f2 = f1;
+    f2.a_src = hq;
+    f2.ascale = hs;
+    f2.w = reinterpret_cast<const char*>(w2);
+    f2.wscale = w2_scale;
+    f2.out = static_cast<char*>(fc2_out);
+    f2.out_scale = nullptr;
+    f2.N = H; f2.K = I; f2.out_ld = H;
+    moe_status st = run_classes_a8<FC1>(f1, R, s, MOE_KID_FC1);
+    if (st != MOE_OK) return st;
+    return run_classes_a8<FC2>(f2, R, s, MOE_KID_FC2);
+}
 
 size_t ffn_scratch_bytes(int T, int k, int n_shared, int I, int act)
 {

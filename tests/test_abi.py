@@ -100,6 +100,31 @@ def test_expert_ffn_validation(L):
     assert f(1, 0, 128, 1) == INVALID
 
 
+def test_quantize_fp8_validation(L):
+    p = C.c_void_p(16)
+    q = L.moe_quantize_fp8
+    assert q(p, 1, 4, 200, p, p, None) == UNSUPPORTED     # cols % 128
+    assert q(p, 2, 4, 256, p, p, None) == INVALID         # fp8 input
+    assert q(p, 1, -1, 256, p, p, None) == INVALID        # rows < 0
+    assert q(p, 1, 4, 0, p, p, None) == INVALID           # cols = 0
+    assert q(p, 1, 4, 256, None, p, None) == INVALID      # null output
+    assert q(None, 1, 0, 256, None, None, None) == OK     # no rows: nothing launched
+
+
+def test_expert_ffn_fp8_validation(L):
+    p = C.c_void_p(16)
+    f = lambda T, H, I, s13=p, ws=p, wsb=1 << 30, k=2, E=8: L.moe_expert_ffn_fp8(  # noqa: E731
+        p, p, T, H, I, k, E, 0, p, p, p, p, s13, p, p, ws, wsb, None)
+    assert f(16, 100, 128) == UNSUPPORTED                 # H % 128
+    assert f(16, 128, 96) == UNSUPPORTED                  # I % 128
+    assert f(16, 128, 128, s13=None) == INVALID           # scales required
+    assert f(16, 128, 128, ws=None) == WORKSPACE
+    assert f(16, 128, 128, wsb=16) == WORKSPACE
+    assert f(16, 128, 128, k=9) == INVALID                # k > E
+    assert f(-1, 128, 128) == INVALID
+    assert f(0, 128, 128, ws=None) == OK                  # T = 0: nothing launched
+
+
 def test_finalize_validation(L):
     p = C.c_void_p(16)
     assert L.moe_finalize(p, 1, p, p, 4, 2, 100, 0, p, 1, None) == UNSUPPORTED  # H % 8
@@ -116,6 +141,8 @@ def test_workspace_size_and_strings(L):
     assert b >= (8192 * 8 + 8192) * 2048 * 2     # holds h in bf16
     assert f(64, 2, 8, 0, 256, 512, 0) >= 128 * 512 * 4
     assert f(4, 9, 8, 0, 128, 128, 1) == 0       # invalid: k > E
+    c = f(8192, 8, 256, 1, 7168, 2048, 2)        # fp8 activations: hq + its 1x128 scales
+    assert c >= (8192 * 8 + 8192) * 2048 * (1 + 4 / 128)
     for st in range(5):
         assert L.moe_status_string(st).decode().startswith("MOE_")
     assert "unknown" in L.moe_status_string(77).decode()
