@@ -12,6 +12,9 @@ HBM.  Prints ONE JSON line on stdout (details go to stderr):
              the launch stream, over as many steps again as were timed (the
              timed steps themselves run without the events)
   decode     the same figures for the DeepSeek-V3-shaped decode batch (T=512)
+  fp8_activations  the fp8 x fp8 path (quantise x in 1x128 blocks, fp8 MFMA
+             grouped GEMMs, h quantised in FC1's epilogue) on the same two
+             shapes with fp8 e4m3 weights; its rooflines use the fp8 peak
   cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
              workload on this host's cores (a reported baseline, not a target)
 
@@ -41,32 +44,39 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def fc_work(w, touched_groups, which):
+def fc_work(w, touched_groups, which, fp8_act=False):
     """Algorithmic FLOPs and HBM bytes of one FC1 or FC2 launch.
 
     FC1: 2*R*H*(2I) FLOPs; reads every touched group's w13 (2I*H weights, +
     fp8 scales), each token's activation row once, writes h (R*I).
     FC2: 2*R*I*H FLOPs; reads touched w2 (H*I) and h, writes fc2_out (R*H).
+    With fp8 activations x and h are e4m3 codes plus one fp32 scale per 128
+    values; fc2_out stays bf16.
     """
     wsz = {"f32": 4, "bf16": 2, "fp8": 1}[w.wdt]
     asz = 4 if w.act == "f32" else 2
+    qsz = 1 + 4.0 / 128 if fp8_act else asz   # x and h
     R, H, I, T = w.R, w.H, w.I, w.T
     sc = 4.0 / (128 * 128) if w.wdt == "fp8" else 0.0
     if which == "fc1":
         flops = 2.0 * R * H * 2 * I
-        nbytes = touched_groups * 2 * I * H * (wsz + sc) + T * H * asz + R * I * asz
+        nbytes = touched_groups * 2 * I * H * (wsz + sc) + T * H * qsz + R * I * qsz
     else:
         flops = 2.0 * R * I * H
-        nbytes = touched_groups * H * I * (wsz + sc) + R * I * asz + R * H * asz
+        nbytes = touched_groups * H * I * (wsz + sc) + R * I * qsz + R * H * asz
     return flops, nbytes
 
 
-def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=None):
+def mfma_peak(w, fp8_act=False):
+    return PEAK["fp8" if fp8_act else ("f32" if w.act == "f32" else "bf16")]
+
+
+def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=None, fp8_act=False):
     """Roofline of one grouped GEMM per step.  A grouped GEMM is issued as one
     launch per row class of groups (tile shape); its time per step is the sum
     of those launches, and the algorithmic work is that of the whole GEMM."""
-    flops, nbytes = fc_work(w, touched, which)
-    peak_f = PEAK["f32" if w.act == "f32" else "bf16"]
+    flops, nbytes = fc_work(w, touched, which, fp8_act)
+    peak_f = mfma_peak(w, fp8_act)
     t_f = flops / (peak_f * 1e12)
     t_b = nbytes / (PEAK["hbm"] * 1e9)
     s = ms_per_step * 1e-3
@@ -83,14 +93,14 @@ def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=Non
             "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
 
 
-def grouped_gemm_summary(w, touched, per_kernel):
+def grouped_gemm_summary(w, touched, per_kernel, fp8_act=False):
     """FC1 + FC2 together: the layer's expert-FFN FLOPs (real rows, not padded
     tiles) and algorithmic bytes over the two GEMMs' time per step."""
-    f1, b1 = fc_work(w, touched, "fc1")
-    f2, b2 = fc_work(w, touched, "fc2")
+    f1, b1 = fc_work(w, touched, "fc1", fp8_act)
+    f2, b2 = fc_work(w, touched, "fc2", fp8_act)
     ms = per_kernel["fc1"] + per_kernel["fc2"]
     s = ms * 1e-3
-    peak_f = PEAK["f32" if w.act == "f32" else "bf16"]
+    peak_f = mfma_peak(w, fp8_act)
     return {"ms_per_step": round(ms, 4), "algorithmic_flops": f1 + f2,
             "algorithmic_bytes": b1 + b2, "tflops": round((f1 + f2) / s / 1e12, 2),
             "gbps": round((b1 + b2) / s / 1e9, 1),
@@ -161,16 +171,18 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
     print(json.dumps(out, indent=1))
 
 
-def run_workload(name, steps, warmup, device):
+def run_workload(name, steps, warmup, device, fp8_act=False):
     import torch
     import mixture_experts_layer_07_amd as moe
     from mixture_experts_layer_07_amd import workloads as wl
 
-    w = wl.WORKLOADS[name]
+    w = wl.get(name)
     t0 = time.time()
     inp = wl.make_inputs(w, 0, device)
-    layer = moe.layer_for_workload(w, device)
+    layer = moe.layer_for_workload(w, device, fp8_act=fp8_act)
     torch.cuda.synchronize()
+    if fp8_act:
+        name = name + " (fp8 activations)"
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
 
     def step():
@@ -250,6 +262,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--decode-workload", default="dsv3_decode")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--fp8act-workloads", nargs="*", default=["dsv3_prefill_fp8", "dsv3_decode_fp8"],
+                    help="workloads also run on the fp8-activation path (none: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -322,6 +336,28 @@ def main():
             "grouped_gemm": grouped_gemm_summary(dw, d["touched"], d["per_kernel"]),
             "per_kernel_ms": d["per_kernel"],
         }
+        del d
+        torch.cuda.empty_cache()
+    if args.fp8act_workloads:
+        out["fp8_activations"] = {}
+        for name in args.fp8act_workloads:
+            r = run_workload(name, args.steps, args.warmup, dev, fp8_act=True)
+            rw = r["w"]
+            out["fp8_activations"][name] = {
+                "workload": f"{rw.name}: T={rw.T} H={rw.H} E={rw.E}+{rw.n_shared} shared I={rw.I} "
+                            f"top-{rw.k}; x and h quantised to e4m3 in 1x128 blocks, fp8 weights "
+                            f"(128x128 block scales), fp8 MFMA, bf16 output",
+                "value": round(rw.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(r["ms"], 4), "dtype": "fp8 e4m3 x e4m3, fp32 accumulate",
+                "roofline": roofline(rw, r["touched"], r["per_kernel"][DOMINANT],
+                                     launches=r["launches"][DOMINANT], fp8_act=True),
+                "roofline_fc2": roofline(rw, r["touched"], r["per_kernel"]["fc2"], "fc2",
+                                         launches=r["launches"]["fc2"], fp8_act=True),
+                "grouped_gemm": grouped_gemm_summary(rw, r["touched"], r["per_kernel"], fp8_act=True),
+                "per_kernel_ms": r["per_kernel"],
+            }
+            del r
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

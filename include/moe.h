@@ -163,6 +163,8 @@ moe_status moe_permute(const int32_t* ids, int T, int k, int E, int n_shared,
  *             (unweighted).
  *  ws         device workspace (moe_workspace_size bytes) holding h.
  * Accumulation is fp32; h and fc2_out are rounded once to `act`.
+ * Limits (MOE_ERR_UNSUPPORTED beyond): x, h [T*k + n_shared*T, I] and one
+ * expert's w13 each below 4 GiB (the kernels use 32-bit byte offsets).
  */
 moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, int E,
                           int n_shared, const int32_t* expert_offsets,
@@ -227,7 +229,8 @@ moe_status moe_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* 
  *             [R, I] at byte 0 (R = T*k + n_shared*T, rows in permuted order)
  *             and their fp32 scales [R, I/128] from the next 256-byte
  *             boundary.
- * H and I are multiples of 128; other arguments as for moe_expert_ffn.
+ * H and I are multiples of 128; xq, hq and one expert's w13 below 4 GiB;
+ * other arguments as for moe_expert_ffn.
  */
 moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H, int I, int k,
                               int E, int n_shared, const int32_t* expert_offsets,

@@ -103,6 +103,16 @@ namespace {
 bool valid_act(int d) { return d == MOE_F32 || d == MOE_BF16; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The GEMM kernels address activation rows, h rows and one group's weights
+// with 32-bit byte offsets from a scalar base.
+bool gemm_offsets_fit(int T, int k, int n_shared, int H, int I, int asz, int wsz)
+{
+    const unsigned long long lim = 1ull << 32;
+    const unsigned long long R = (unsigned long long)T * k + (unsigned long long)n_shared * T;
+    return (unsigned long long)T * H * asz < lim && R * I * asz < lim &&
+           2ull * I * H * wsz < lim;
+}
+
 moe_status check_common(int T, int k, int E, int n_shared)
 {
     if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
@@ -219,6 +229,8 @@ moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, in
         return set_error(MOE_ERR_UNSUPPORTED, "bf16 activations need bf16 or fp8 weights");
     if (wdt == MOE_FP8_E4M3 && (!w13_scale || !w2_scale))
         return set_error(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+    if (!gemm_offsets_fit(T, k, n_shared, H, I, act == MOE_F32 ? 4 : 2, wdt == MOE_F32 ? 4 : wdt == MOE_BF16 ? 2 : 1))
+        return set_error(MOE_ERR_UNSUPPORTED, "x, h or one expert's weights exceed 4 GiB (T=%d, H=%d, I=%d)", T, H, I);
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !w13 || !w2 || !fc2_out || (E > 0 && !permuted_pair))
         return set_error(MOE_ERR_INVALID_ARG, "x, expert_offsets, permuted_pair, w13, w2 and fc2_out must be non-null");
@@ -254,6 +266,8 @@ moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, in
     if (H < 1 || I < 1) return set_error(MOE_ERR_INVALID_ARG, "H and I must be positive (H=%d, I=%d)", H, I);
     if (H % 128 || I % 128)
         return set_error(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (H=%d, I=%d)", H, I);
+    if (!gemm_offsets_fit(T, k, n_shared, H, I, 1, 1))
+        return set_error(MOE_ERR_UNSUPPORTED, "xq, hq or one expert's weights exceed 4 GiB (T=%d, H=%d, I=%d)", T, H, I);
     if (T == 0) return MOE_OK;
     if (!xq || !x_scale || !expert_offsets || !w13 || !w2 || !w13_scale || !w2_scale || !fc2_out ||
         (E > 0 && !permuted_pair))

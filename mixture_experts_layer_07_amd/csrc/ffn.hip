@@ -512,23 +512,33 @@ __device__ __forceinline__ void wait_vmcnt_le(int n)
 }
 
 // One 16-byte-per-lane global->LDS transfer into the 1 KB at LDS byte address
-// `lds_addr` (wave-uniform).  Written as inline asm on purpose: the compiler's
+// `lds_addr` (wave-uniform), from `base` (wave-uniform, scalar registers) plus
+// a 32-bit per-lane byte offset.  Written as inline asm on purpose: the compiler's
 // own tracking of LDS DMA inserts a full vmcnt(0) wait before every later LDS
 // read, which would drain the ring each slice; the kernel instead waits for
 // exactly the stage it needs (wait_vmcnt) before the barrier that publishes it.
 // M0 is reserved by the compiler and used by nothing else in this kernel.
-__device__ __forceinline__ void dma16(unsigned lds_addr, const char* src)
+__device__ __forceinline__ void dma16(unsigned lds_addr, const char* base, uint32_t off)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
 }
 
 // Same with 4 bytes per lane: lane l lands at byte 4*l of the 256 bytes at
 // `lds_addr`.
-__device__ __forceinline__ void dma4(unsigned lds_addr, const char* src)
+__device__ __forceinline__ void dma4(unsigned lds_addr, const char* base, uint32_t off)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -643,7 +653,9 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         // the LDS-only barriers wait for it
         return *(const __attribute__((address_space(1))) int*)(a.permuted_pair + i);
     };
-    auto source = [&](const TileInfo& ti, int q, int raw) -> const char* {
+    // Per-lane byte offset of op q's source from its base: the activations
+    // (a_src), this tile's group of weights (wbase) or the activation scales.
+    auto source = [&](const TileInfo& ti, int q, int raw) -> uint32_t {
         if (op_is_s(q)) {
             const int rr = ti.m0 + s_row;
             long r;
@@ -653,10 +665,10 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             } else {
                 r = ti.row0 + (rr < ti.nrows ? rr : 0);
             }
-            return reinterpret_cast<const char*>(a.ascale + (size_t)r * (a.K / 128));
+            return (uint32_t)(r * (a.K / 128) * 4);
         }
         const int row = op_row(q);
-        const char* p;
+        uint32_t p;
         if (op_is_a(q)) {
             const int rr = ti.m0 + row;
             long r;
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             } else {
                 r = ti.row0 + (rr < ti.nrows ? rr : 0);
             }
-            p = a.a_src + (size_t)r * a_ld;
+            p = (uint32_t)(r * a_ld);
         } else {
             const int j = row;
             int wrow;
@@ -677,19 +689,23 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             } else {
                 wrow = min(ti.nt * C::BN + j, a.N - 1);  // partial last N-tile
             }
-            p = a.w + ((size_t)ti.g * a.N + wrow) * w_ld;
+            p = (uint32_t)(wrow * w_ld);
         }
         return p + op_chunk(q, row) * 16;
     };
-    const char* src[C::IPW];
+    auto group_weights = [&](const TileInfo& ti) { return uniform_ptr(a.w + (size_t)ti.g * a.N * w_ld); };
+    const char* abase = uniform_ptr(a.a_src);
+    const char* sbase = uniform_ptr(reinterpret_cast<const char*>(a.ascale));
+    const char* wbase;  // weights of the group whose slices `issue` sends
+    uint32_t src[C::IPW];
     auto issue = [&](int st, int kt) {
 #pragma unroll
         for (int q = 0; q < C::IPW_AB; ++q)
             dma16(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + (q * C::NW + wave) * 1024),
-                  src[q] + (size_t)kt * (op_is_a(q) ? 128 : C::BROWB));
+                  op_is_a(q) ? abase : wbase, src[q] + (uint32_t)kt * (op_is_a(q) ? 128u : (uint32_t)C::BROWB));
         if constexpr (C::A8)
             dma4(__builtin_amdgcn_readfirstlane(lds_base + st * C::STAGE + C::A_BYTES + C::B_BYTES + wave * 256),
-                 src[C::IPW_AB] + (size_t)kt * 4);
+                 sbase, src[C::IPW_AB] + (uint32_t)kt * 4u);
     };
     // this wave's transfers of a slice have landed while `later` newer slices'
     // transfers (IPW each) may still be in flight
@@ -702,6 +718,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         for (int q = 0; q < C::IPW; ++q) idx[q] = a_raw(cur, q);
 #pragma unroll
         for (int q = 0; q < C::IPW; ++q) src[q] = source(cur, q, idx[q]);
+        wbase = group_weights(cur);
     }
     int ring = 0;  // ring slot of the current tile's slice 0
 #pragma unroll
@@ -761,13 +778,43 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                     sa[mi] = *reinterpret_cast<const f32x4_t*>(lsa + mi * 16 + g4 * 4);
                     fa[mi] = lds_row32(la, wm * C::WTM + mi * 16 + (lane & 15), g4);
                 }
+                // Software pipeline: the VALU that scales MFMA result j runs
+                // after MFMA j+2 has been issued, so it does not wait for j.
+                // scale products per slice where the registers allow: FC2 has one
+                // weight block per wave (sa becomes sa * sw); FC1 two (gate, up),
+                // precomputed for 64x64 wave tiles, applied per MFMA otherwise
+                constexpr bool PRE1 = C::MI * C::NI <= 16;
+                f32x4_t su[PRE1 ? C::MI : 1];
+                if (MODE == FC1 && PRE1) {
 #pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni) {
-                    const i32x8_t fb = lds_row32(lb, wn * C::WTN + ni * 16 + (lane & 15), g4);
-                    const float sw = (ni & 1) ? sw1 : sw0;
+                    for (int mi = 0; mi < C::MI; ++mi) su[mi] = sa[mi] * sw1;
+                }
+                if (MODE == FC2 || PRE1) {
 #pragma unroll
-                    for (int mi = 0; mi < C::MI; ++mi)
-                        acc[mi][ni] += sa[mi] * (sw * mfma_fp8(fa[mi], fb));
+                    for (int mi = 0; mi < C::MI; ++mi) sa[mi] *= sw0;
+                }
+                constexpr int NB = C::MI * C::NI, LAGB = 2;
+                f32x4_t pr[LAGB + 1];
+                i32x8_t fb[2];
+                fb[0] = lds_row32(lb, wn * C::WTN + (lane & 15), g4);
+#pragma unroll
+                for (int j = 0; j < NB + LAGB; ++j) {
+                    if (j < NB) {
+                        const int mi = j % C::MI, ni = j / C::MI;
+                        if (mi == 0 && ni + 1 < C::NI)
+                            fb[(ni + 1) & 1] = lds_row32(lb, wn * C::WTN + (ni + 1) * 16 + (lane & 15), g4);
+                        pr[j % (LAGB + 1)] = mfma_fp8(fa[mi], fb[ni & 1]);
+                    }
+                    if (j >= LAGB) {
+                        const int jj = j - LAGB, mi = jj % C::MI, ni = jj / C::MI;
+                        if (MODE == FC2)
+                            acc[mi][ni] += sa[mi] * pr[jj % (LAGB + 1)];
+                        else if constexpr (PRE1)
+                            acc[mi][ni] += ((ni & 1) ? su[mi % (PRE1 ? C::MI : 1)] : sa[mi]) * pr[jj % (LAGB + 1)];
+                        else
+                            acc[mi][ni] += sa[mi] * (((ni & 1) ? sw1 : sw0) * pr[jj % (LAGB + 1)]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
 #pragma unroll
@@ -836,6 +883,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         if (has_next) {
 #pragma unroll
             for (int q = 0; q < C::IPW; ++q) src[q] = source(nxt, q, nidx[q]);
+            wbase = group_weights(nxt);
             ring = (ring + nk) % C::S;
 #pragma unroll
             for (int st = 0; st < C::S - 1; ++st)

@@ -103,6 +103,20 @@ WORKLOADS = {
     ]
 }
 
+# The DeepSeek-V3 shapes with fp8 e4m3 weights (same seeds and substreams as
+# the bf16 ones; weights quantised per 128x128 block): the shapes on which the
+# fp8-activation path is measured beside the bf16 headline.
+FP8_WORKLOADS = {
+    "dsv3_decode_fp8": WORKLOADS["dsv3_decode"].with_(name="dsv3_decode_fp8", wdt="fp8"),
+    "dsv3_prefill_fp8": WORKLOADS["dsv3_prefill"].with_(name="dsv3_prefill_fp8", wdt="fp8"),
+}
+
+
+def get(name: str) -> Workload:
+    """A workload of WORKLOADS or FP8_WORKLOADS by name."""
+    return WORKLOADS[name] if name in WORKLOADS else FP8_WORKLOADS[name]
+
+
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16,
                "fp8": torch.float8_e4m3fn}
 FP8_MAX = 448.0

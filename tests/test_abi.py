@@ -98,6 +98,10 @@ def test_expert_ffn_validation(L):
     assert f(1, 128, 128, 1, ws=None) == WORKSPACE
     assert f(1, 128, 128, 1, wsb=16) == WORKSPACE
     assert f(1, 0, 128, 1) == INVALID
+    big = lambda T, H, I: L.moe_expert_ffn(  # noqa: E731
+        p, 1, T, H, I, 8, 256, 1, p, p, p, p, 1, None, None, p, p, 1 << 62, None)
+    assert big(262144, 7168, 2048) == UNSUPPORTED          # h: 2.4M rows x 2048 bf16 > 4 GiB
+    assert "4 GiB" in err(L)
 
 
 def test_quantize_fp8_validation(L):
@@ -123,6 +127,7 @@ def test_expert_ffn_fp8_validation(L):
     assert f(16, 128, 128, k=9) == INVALID                # k > E
     assert f(-1, 128, 128) == INVALID
     assert f(0, 128, 128, ws=None) == OK                  # T = 0: nothing launched
+    assert f(600000, 7168, 2048, k=8, E=256) == UNSUPPORTED  # hq: 4.8M rows x 2048 > 4 GiB
 
 
 def test_finalize_validation(L):

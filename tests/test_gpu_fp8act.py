@@ -236,11 +236,7 @@ def sample_tokens(T, ids, E, n=16, seed=0):
     return np.array(sorted(pick), np.int32)
 
 
-FP8ACT_WORKLOADS = {
-    "qwen3_fp8": wl.WORKLOADS["qwen3_fp8"],
-    "dsv3_decode_fp8": wl.WORKLOADS["dsv3_decode"].with_(name="dsv3_decode_fp8", wdt="fp8"),
-    "dsv3_prefill_fp8": wl.WORKLOADS["dsv3_prefill"].with_(name="dsv3_prefill_fp8", wdt="fp8"),
-}
+FP8ACT_WORKLOADS = {"qwen3_fp8": wl.WORKLOADS["qwen3_fp8"], **wl.FP8_WORKLOADS}
 
 
 @pytest.mark.parametrize("name", list(FP8ACT_WORKLOADS))
