@@ -60,7 +60,31 @@ struct FfnArgs {
     int K;                     // reduction length (FC1: H, FC2: I)
     int out_ld;                // FC1: I, FC2: H
     int lo_rows, hi_rows;      // this launch serves groups with lo <= rows < hi
+    // Remainder hand-off between row classes: a launch whose own group ends in
+    // a partial tile of at most give_max rows leaves those rows out; the launch
+    // with take_max > 0 serves them for groups of [take_lo, take_hi) (whose
+    // tile height was take_bm).  0 = no hand-off.
+    int give_max;
+    int take_lo, take_hi, take_bm, take_max;
 };
+
+// Rows [beg, end) of a group of n rows that a launch with tile height bm
+// serves (see FfnArgs); beg == end when it serves none.
+struct RowWindow {
+    int beg, end;
+};
+__device__ __forceinline__ RowWindow row_window(const FfnArgs& a, int n, int bm)
+{
+    if (n >= a.lo_rows && n < a.hi_rows && n > 0) {
+        const int r = n % bm;
+        return {0, (a.give_max > 0 && n >= bm && r >= 1 && r <= a.give_max) ? n - r : n};
+    }
+    if (a.take_max > 0 && n >= a.take_lo && n < a.take_hi && n >= a.take_bm) {
+        const int r = n % a.take_bm;
+        if (r >= 1 && r <= a.take_max) return {n - r, n};
+    }
+    return {0, 0};
+}
 
 constexpr int kRowBytes = 128;                 // K slice per row, bytes
 constexpr int kLdsStride = kRowBytes;          // LDS row (no pad: XOR-swizzled chunks)
@@ -188,13 +212,15 @@ __device__ __forceinline__ void lstore(char* lds, const u32x4_t (&ra)[C::A_CH],
 }
 
 // Tile of the flattened work list, decoded.
+// nrows: end of the rows this launch serves in group g (rows >= nrows of a
+// tile are padding); m0: first row of the tile within the group.
 struct TileInfo {
     int g, row0, nrows, m0, nt;
 };
 
 template <class C>
-__device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_off, const int* s_tile0,
-                                                int G, int ntiles_n)
+__device__ __forceinline__ TileInfo decode_tile(const FfnArgs& a, int tile, const int* s_off,
+                                                const int* s_tile0, int G, int ntiles_n)
 {
     // every value here is block-uniform; readfirstlane keeps them in SGPRs
     int lo = 0, hi = G - 1;
@@ -205,8 +231,9 @@ __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_off, cons
     TileInfo ti;
     ti.g = lo;
     ti.row0 = __builtin_amdgcn_readfirstlane(s_off[lo]);
-    ti.nrows = __builtin_amdgcn_readfirstlane(s_off[lo + 1]) - ti.row0;
-    const int mtiles = (ti.nrows + C::BM - 1) / C::BM;
+    const RowWindow win = row_window(a, __builtin_amdgcn_readfirstlane(s_off[lo + 1]) - ti.row0, C::BM);
+    ti.nrows = win.end;
+    const int mtiles = (win.end - win.beg + C::BM - 1) / C::BM;
     // group-M order: runs of GM M-tiles share one N-tile, so a contiguous slice
     // of the list reuses both operands (A across N-tiles, B across M-tiles)
     const int local = tile - __builtin_amdgcn_readfirstlane(s_tile0[lo]);
@@ -214,7 +241,7 @@ __device__ __forceinline__ TileInfo decode_tile(int tile, const int* s_off, cons
     const int first_m = band * C::GM;
     const int gm = min(mtiles - first_m, C::GM);
     const int r = local - band * C::GM * ntiles_n;
-    ti.m0 = (first_m + r % gm) * C::BM;
+    ti.m0 = win.beg + (first_m + r % gm) * C::BM;
     ti.nt = r / gm;
     return ti;
 }
@@ -284,7 +311,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
         const int g0 = lane * per, g1 = min(G, g0 + per);
         auto ntiles = [&](int g) {
             const int n = s_off[g + 1] - s_off[g];
-            return (n >= a.lo_rows && n < a.hi_rows && n > 0) ? (n + C::BM - 1) / C::BM * ntiles_n : 0;
+            const RowWindow w = row_window(a, n, C::BM);
+            return (w.end - w.beg + C::BM - 1) / C::BM * ntiles_n;
         };
         int sum = 0;
         for (int g = g0; g < g1; ++g) sum += ntiles(g);
@@ -316,7 +344,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
     const char* b_ptr[C::B_CH];
     u32x4_t ra[C::A_CH], rb[C::B_CH];
 
-    TileInfo cur = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
+    TileInfo cur = decode_tile<C>(a, tile, s_off, s_tile0, G, ntiles_n);
     tile_pointers<AT, WT, MODE, C>(a, cur, tid, a_ptr, a_ok, b_ptr);
     gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, 0);
     lstore<C>(lds, ra, rb, tid, 0);
@@ -340,7 +368,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
             if (kt + 1 < nk) {
                 gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, kt + 1);
             } else if (has_next) {
-                nxt = decode_tile<C>(next_tile, s_off, s_tile0, G, ntiles_n);
+                nxt = decode_tile<C>(a, next_tile, s_off, s_tile0, G, ntiles_n);
                 tile_pointers<AT, WT, MODE, C>(a, nxt, tid, a_ptr, a_ok, b_ptr);
                 gload<C, WT>(ra, rb, a_ptr, a_ok, b_ptr, 0);
             } else {
@@ -592,7 +620,8 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         const int g0 = lane * per, g1 = min(G, g0 + per);
         auto ntiles = [&](int g) {
             const int n = s_off[g + 1] - s_off[g];
-            return (n >= a.lo_rows && n < a.hi_rows && n > 0) ? (n + C::BM - 1) / C::BM * ntiles_n : 0;
+            const RowWindow w = row_window(a, n, C::BM);
+            return (w.end - w.beg + C::BM - 1) / C::BM * ntiles_n;
         };
         int sum = 0;
         for (int g = g0; g < g1; ++g) sum += ntiles(g);
@@ -711,7 +740,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
     // transfers (IPW each) may still be in flight
     auto wait_stage = [&](int later) { wait_vmcnt_le<(C::S - 2) * C::IPW>(later * C::IPW); };
 
-    TileInfo cur = decode_tile<C>(tile, s_off, s_tile0, G, ntiles_n);
+    TileInfo cur = decode_tile<C>(a, tile, s_off, s_tile0, G, ntiles_n);
     {
         int idx[C::IPW];
 #pragma unroll
@@ -731,7 +760,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
         TileInfo nxt = cur;
         int nidx[C::IPW];
         if (has_next) {
-            nxt = decode_tile<C>(next_tile, s_off, s_tile0, G, ntiles_n);
+            nxt = decode_tile<C>(a, next_tile, s_off, s_tile0, G, ntiles_n);
 #pragma unroll
             for (int q = 0; q < C::IPW; ++q) nidx[q] = a_raw(nxt, q);
         }
@@ -986,7 +1015,9 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
 }
 
 template <int MODE, class C>
-moe_status run_dma_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s, int kid)
+moe_status run_dma_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s, int kid,
+                        int give_max = 0, int take_lo = 0, int take_hi = 0, int take_bm = 0,
+                        int take_max = 0)
 {
     auto kern = dma_gemm_kernel<MODE, C>;
     static int occ = -1;
@@ -997,6 +1028,11 @@ moe_status run_dma_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream
     }
     args.lo_rows = lo_rows;
     args.hi_rows = hi_rows;
+    args.give_max = give_max;
+    args.take_lo = take_lo;
+    args.take_hi = take_hi;
+    args.take_bm = take_bm;
+    args.take_max = take_max;
     const long max_tiles = (long)(R / C::BM + args.G) * ((args.N + C::BN - 1) / C::BN);
     long grid = (long)device_cu_count() * occ;
     if (grid > max_tiles) grid = max_tiles;
@@ -1040,17 +1076,36 @@ moe_status run_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s
 constexpr int kMidRows = 64;
 constexpr int kBigRows = 384;
 constexpr int kAllRows = 1 << 30;
+constexpr int kHandoffMinK = 4096;  // remainder hand-off between classes from this K on
 
 // bf16 activations with bf16 or fp8 weights: every row class on the
 // direct-to-LDS engine.
+//
+// A group's last, partial tile goes to the next smaller shape when it is at
+// most one tile of that shape: a big group ending in <= 128 rows past its
+// last full 256-row tile hands them to the mid launch (when the big tiles are
+// 256 rows high), a mid group ending in <= 32 rows past a full 128-row tile
+// to the skinny launch.  The hand-off
+// replaces a mostly-padding tile with one of a quarter / half the MFMA work
+// (the weight tile is read once either way).
 template <int MODE, class Skinny, class Mid, class Big>
 moe_status run_classes_dma(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
-    moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid);
+    static_assert(Skinny::BM < Mid::BM && Mid::BM <= Big::BM, "tile heights grow with the class");
+    // Only for long K: a tile's fixed costs (ring fill, epilogue) are then small
+    // against its MFMA work, so a shorter tile pays.  Measured: FC2 of the
+    // Mixtral-shaped layer (K = 14336) -10%, FC1 of the fp8 x fp8 DeepSeek-V3
+    // prefill (K = 7168) -2.5%; with K = 2048 (DeepSeek-V3 FC2) +2.5%.
+    const bool handoff = f.K >= kHandoffMinK;
+    const int mid_give = handoff ? Skinny::BM : 0;
+    const int big_give = (handoff && Big::BM > Mid::BM) ? Mid::BM : 0;  // none when the shapes match
+    moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid, 0, kMidRows, kBigRows,
+                                               Mid::BM, mid_give);
     if (st != MOE_OK) return st;
-    st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid);
+    st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid, mid_give, kBigRows, kAllRows,
+                                 Big::BM, big_give);
     if (st != MOE_OK) return st;
-    return run_dma_gemm<MODE, Big>(f, kBigRows, kAllRows, R, s, kid);
+    return run_dma_gemm<MODE, Big>(f, kBigRows, kAllRows, R, s, kid, big_give);
 }
 
 // Shapes chosen by measurement on MI355X: 4 waves per SIMD for the large tiles

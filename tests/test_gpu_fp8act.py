@@ -3,8 +3,9 @@ against the CPU oracle, through the C ABI.
 
 Bars: codes and scales of the 1x128 quantiser bit-exact; FFN rows and layer
 output within relative L2 1e-2 (per row 5e-2); the quantised h in the
-workspace: scales within 1e-4 relative, every code a correct rounding of the
-oracle's h up to 1e-4 of its block maximum.  The oracle quantises x the
+workspace: scales within 1e-3 relative, every code a correct rounding of the
+oracle's h up to 1e-3 of its block maximum (one fp8 MFMA sums its 128
+products with ~13-bit precision).  The oracle quantises x the
 same way (bit-exact, checked first) and quantises its fp64 h rounded to fp32;
 the GPU quantises its fp32-accumulated h, so the codes of h differ only where
 an fp32 rounding difference crosses an e4m3 rounding midpoint (rare), and the
@@ -115,18 +116,21 @@ def fp8_workload(T, H, I, E, k, n_shared=0, method=4, **kw):
 def check_h_codes(w, ws, h_ref):
     """The quantised intermediate left in the workspace (hq [R, I] e4m3 at 0,
     its scales [R, I/128] at the next 256-byte boundary) against the oracle's
-    fp64 h: the scales match fl32(amax/448) of the oracle's h within fp32
-    noise, and every GPU code is a round-to-nearest e4m3 code of a value within
-    1e-4 of the block maximum of the oracle's h (the GPU's h carries fp32
-    accumulation error).  Returns the fraction of codes that differ from the
-    oracle's own quantisation."""
+    fp64 h.  One fp8 MFMA sums its 128 products with ~13-bit precision
+    (measured on MI355X: error up to 1.7e-4 of the sum of |products|), and
+    the GPU adds one such sum per 128-wide K block, so its h (and the block
+    maximum) can differ from the oracle's by ~1e-4 relative: the scales must
+    match within 1e-3, and every GPU code must be a round-to-nearest e4m3
+    code of a value within 1e-3 of the block maximum of the oracle's h.
+    Returns the fraction of codes that differ from the oracle's own
+    quantisation."""
     R, I = w.R, w.I
     hq = host(ws[:R * I]).numpy().reshape(R, I)
     off = (R * I + 255) // 256 * 256
     hs = host(ws[off:off + R * (I // 128) * 4]).numpy().view(np.float32).reshape(R, I // 128)
     qo, so = oracle.quantize_fp8(h_ref.astype(np.float32), "f32")
     rel = np.abs(hs.astype(np.float64) - so) / np.maximum(so, 1e-30)
-    assert rel.max() < 1e-4, f"h scale rel diff {rel.max()}"
+    assert rel.max() < 1e-3, f"h scale rel diff {rel.max()}"
     table = np.array([oracle.decode_e4m3(c) for c in range(256)])
     s_g = np.repeat(hs.astype(np.float64), 128, axis=1)
     v = table[hq] * s_g
@@ -134,9 +138,9 @@ def check_h_codes(w, ws, h_ref):
     m = np.maximum(np.abs(v), np.abs(h_ref)) / np.maximum(s_g, 1e-300)
     step = np.where(m >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(m, 2.0 ** -6))) - 3), 2.0 ** -9)
     err = np.abs(v - h_ref)
-    allowed = step / 2 * s_g * (1 + 1e-6) + 1e-4 * amax
+    allowed = step / 2 * s_g * (1 + 1e-6) + 1e-3 * amax
     bad = err > allowed
-    assert not bad.any(), f"{int(bad.sum())} h codes off by more than rounding + 1e-4 of the block max"
+    assert not bad.any(), f"{int(bad.sum())} h codes off by more than rounding + 1e-3 of the block max"
     return float((hq != qo).mean())
 
 
@@ -185,21 +189,33 @@ def test_expert_ffn_fp8_parity_small(shape):
     assert err < TOL and row_err.max() < ROW_TOL, (err, row_err.max())
 
 
-CLASS_EDGE_ROWS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 513]
+CLASS_EDGE_ROWS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 161, 255, 256, 257, 383, 384, 385, 511,
+                   512, 513, 640, 641]
 
 
-def test_expert_ffn_fp8_row_class_boundaries():
+@pytest.mark.parametrize("H,I", [(256, 384), (4096, 256), (256, 4096)])
+def test_expert_ffn_fp8_row_class_boundaries(H, I):
+    # (4096, 256) / (256, 4096): FC1 / FC2 with K >= 4096, where a group's last
+    # partial tile is handed to the next smaller tile shape
     counts = CLASS_EDGE_ROWS
     E = len(counts)
     T = sum(counts)
-    w = fp8_workload(T, 256, 384, E, 1, method=0)
+    w = fp8_workload(T, H, I, E, 1, method=0)
     inp = wl.make_inputs(w, 4)
     owner = np.repeat(np.arange(E), counts)
     np.random.default_rng(4).shuffle(owner)
     logits = torch.full((T, E), -5.0)
     logits[torch.arange(T), torch.from_numpy(owner)] = 5.0
     inp["logits"] = logits
-    err, got, ref = run_ffn_fp8_check(w, inp)
+    rows = None
+    if H * I > 256 * 384:
+        off = np.concatenate([[0], np.cumsum(counts)])
+        sel = set()
+        for g in range(E):
+            sel.update(range(off[g], min(off[g] + 40, off[g + 1])))
+            sel.update(range(max(off[g + 1] - 40, off[g]), off[g + 1]))
+        rows = np.array(sorted(sel), np.int32)
+    err, got, ref = run_ffn_fp8_check(w, inp, rows)
     row_err = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
     assert err < TOL and row_err.max() < ROW_TOL, (err, row_err.max())
 
