@@ -300,3 +300,46 @@ def test_layer_fp8act_determinism_and_nan_poison():
         assert not torch.isnan(y).any()
         outs.append(y.clone())
     assert torch.equal(outs[0], outs[1])
+
+
+def test_layer_fp8act_graph_capture_replays():
+    """route, permute, quantize_fp8, expert_ffn_fp8 and finalize captured into
+    one HIP graph replay to the eager result bit for bit, also after the
+    captured input buffers are refilled between replays."""
+    w = fp8_workload(700, 256, 256, 16, 4, n_shared=1, method=2, n_group=4, topk_group=2,
+                     scaling=2.5, bias=True)
+    layer = moe.layer_for_workload(w, DEV, fp8_act=True)
+    inputs = [{k: (None if v is None else v.to(DEV)) for k, v in wl.make_inputs(w, s).items()}
+              for s in (11, 12)]
+    g = {k: (None if v is None else v.clone()) for k, v in inputs[0].items()}
+    fwd = lambda: layer(g["x"], g["logits"], g["w13"], g["w2"], g["bias"],  # noqa: E731
+                        g["w13_scale"], g["w2_scale"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y_graph = fwd()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = inputs[rep % 2]
+        for k, v in src.items():
+            if v is not None:
+                g[k].copy_(v)
+        torch.cuda.synchronize()
+        eager = layer(src["x"], src["logits"], src["w13"], src["w2"], src["bias"],
+                      src["w13_scale"], src["w2_scale"]).clone()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph.view(torch.int16), eager.view(torch.int16)), rep
+    x1 = host(inputs[1]["x"])
+    ids, sc, _ = oracle.route(host(inputs[1]["logits"]), w.k, w.method, w.n_group, w.topk_group,
+                              host(inputs[1]["bias"]), w.scaling, False)
+    qo, so = oracle_quantize(x1)
+    W = oracle.Weights(host(g["w13"]), host(g["w2"]), "fp8", host(g["w13_scale"]), host(g["w2_scale"]))
+    toks = np.arange(0, w.T, 7, dtype=np.int32)
+    ref = oracle.layer_tokens(W, qo, "fp8", w.T, w.k, w.E, 1, ids, sc, toks, x_scale=so)
+    assert rel_l2(host(y_graph).double().numpy()[toks], ref) < TOL
