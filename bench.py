@@ -17,6 +17,9 @@ HBM.  Prints ONE JSON line on stdout (details go to stderr):
              shapes with fp8 e4m3 weights; its rooflines use the fp8 peak
   cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
              workload on this host's cores (a reported baseline, not a target)
+  calibration  attainable peaks measured in the same run with library kernels
+             (a 1 GiB device copy; 8192^3 bf16 and fp8 GEMMs of torch/hipBLASLt
+             on random data); each roofline also reports its fraction of these
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -101,8 +104,10 @@ def grouped_gemm_summary(w, touched, per_kernel, fp8_act=False):
     ms = per_kernel["fc1"] + per_kernel["fc2"]
     s = ms * 1e-3
     peak_f = mfma_peak(w, fp8_act)
+    routed = (f1 + f2) * w.P / w.R  # FLOPs of the routed rows only (shared rows excluded)
     return {"ms_per_step": round(ms, 4), "algorithmic_flops": f1 + f2,
             "algorithmic_bytes": b1 + b2, "tflops": round((f1 + f2) / s / 1e12, 2),
+            "routed_only_tflops": round(routed / s / 1e12, 2),
             "gbps": round((b1 + b2) / s / 1e9, 1),
             "mfma_frac": round((f1 + f2) / s / 1e12 / peak_f, 4),
             "hbm_frac": round((b1 + b2) / s / 1e9 / PEAK["hbm"], 4)}
@@ -119,6 +124,64 @@ def load_traffic(workload):
     if d.get("kernel_source_sha") != kernel_sha():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def calibrate(device, reps=5):
+    """Measured attainable peaks on this GPU: HBM GB/s of a 1 GiB copy (read +
+    write), bf16 and fp8 dense GEMM TFLOP/s of the vendor library at 8192^3 on
+    N(0,1) data (fp8 through torch._scaled_mm with unit scales; None when the
+    build has no fp8 GEMM)."""
+    import torch
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=device).random_()
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    out["hbm_copy_gbps"] = round(2 * src.numel() / best(lambda: dst.copy_(src)) / 1e9, 1)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+    out["bf16_gemm_tflops"] = round(2.0 * n ** 3 / best(lambda: torch.matmul(a, b)) / 1e12, 1)
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=device, dtype=torch.float32)
+        out["fp8_gemm_tflops"] = round(2.0 * n ** 3 / best(
+            lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)) / 1e12, 1)
+    except Exception as e:  # noqa: BLE001 - report what the build lacks
+        out["fp8_gemm_tflops"] = None
+        log(f"[bench] fp8 calibration GEMM unavailable: {type(e).__name__}: {e}")
+    del a, b
+    torch.cuda.empty_cache()
+    out["method"] = ("best of 5: torch copy_ of 1 GiB (2 GiB moved), torch.matmul bf16 8192^3, "
+                     "torch._scaled_mm e4m3 8192^3 (unit scales), N(0,1) operands")
+    return out
+
+
+def add_calibrated(rl, cal, fp8_act=False):
+    """Fraction of the measured peak next to the published one."""
+    if cal is None:
+        return rl
+    if rl["bound"] == "hbm":
+        peak = cal.get("hbm_copy_gbps")
+    else:
+        peak = cal.get("fp8_gemm_tflops" if fp8_act else "bf16_gemm_tflops")
+    rl["calibrated_peak"] = peak
+    rl["frac_of_calibrated"] = round(rl["achieved"] / peak, 4) if peak else None
+    return rl
 
 
 def calibration_copy(mib, device):
@@ -202,11 +265,16 @@ def run_workload(name, steps, warmup, device, fp8_act=False):
     elapsed = time.perf_counter() - t0
     moe.timing_enable(True)
     moe.kernel_times(reset=True)
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
         step()
+        b.record()
     torch.cuda.synchronize()
     kt = moe.kernel_times(reset=True)
     moe.timing_enable(False)
+    step_ms = sorted(a.elapsed_time(b) for a, b in ev)
     cnt = torch.bincount(layer.ids.flatten().long(), minlength=w.E).cpu()
     touched = int((cnt > 0).sum()) + w.n_shared
     ms = elapsed * 1e3 / steps
@@ -217,7 +285,14 @@ def run_workload(name, steps, warmup, device, fp8_act=False):
     log(f"[bench] {name}: rows per expert min {int(cnt.min())} median "
         f"{int(cnt.median())} max {int(cnt.max())}, empty experts {int((cnt == 0).sum())}")
     return dict(w=w, inp=inp, layer=layer, ms=ms, per_kernel=per_kernel, touched=touched,
-                counts=cnt, launches=launches)
+                counts=cnt, launches=launches,
+                step_stats={"median_ms": round(step_ms[len(step_ms) // 2], 4),
+                            "min_ms": round(step_ms[0], 4),
+                            "note": "per-step HIP events in the pass with kernel hooks on"},
+                histogram={"rows_per_expert_min": int(cnt.min()),
+                           "rows_per_expert_median": int(cnt.median()),
+                           "rows_per_expert_max": int(cnt.max()),
+                           "empty_experts": int((cnt == 0).sum())})
 
 
 def cpu_baseline(res, seconds):
@@ -266,6 +341,8 @@ def main():
                     help="workloads also run on the fp8-activation path (none: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measured-peak calibration (copy and library GEMMs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -288,6 +365,9 @@ def main():
 
     if args.calibrate_copy_mib:
         calibration_copy(args.calibrate_copy_mib, dev)
+    cal = None if args.no_calibration else calibrate(dev)
+    if cal:
+        log(f"[bench] calibration {cal}")
     main_res = run_workload(args.workload, args.steps, args.warmup, dev)
     w = main_res["w"]
     traffic = load_traffic(args.workload)
@@ -310,11 +390,14 @@ def main():
                                f"I={w.I} top-{w.k}, route method {w.method}, "
                                f"{w.act} activations, {w.wdt} weights",
                    "global_batch": w.T, "parallelism": "single GPU, all experts local"},
-        "roofline": rl,
-        "roofline_fc2": roofline(w, main_res["touched"], main_res["per_kernel"]["fc2"], "fc2",
-                                 launches=main_res["launches"]["fc2"]),
+        "roofline": add_calibrated(rl, cal),
+        "roofline_fc2": add_calibrated(roofline(w, main_res["touched"], main_res["per_kernel"]["fc2"],
+                                                "fc2", launches=main_res["launches"]["fc2"]), cal),
         "grouped_gemm": grouped_gemm_summary(w, main_res["touched"], main_res["per_kernel"]),
         "per_kernel_ms": main_res["per_kernel"],
+        "step_stats": main_res["step_stats"],
+        "rows_per_expert": main_res["histogram"],
+        "calibration": cal,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
@@ -328,13 +411,15 @@ def main():
             "workload": f"{dw.name}: T={dw.T} H={dw.H} E={dw.E} I={dw.I} top-{dw.k}",
             "value": round(dw.T / (d["ms"] * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(d["ms"], 4),
-            "roofline": roofline(dw, d["touched"], d["per_kernel"][DOMINANT],
-                                 traffic=load_traffic(args.decode_workload),
-                                 launches=d["launches"][DOMINANT]),
-            "roofline_fc2": roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2",
-                                     launches=d["launches"]["fc2"]),
+            "roofline": add_calibrated(roofline(dw, d["touched"], d["per_kernel"][DOMINANT],
+                                                traffic=load_traffic(args.decode_workload),
+                                                launches=d["launches"][DOMINANT]), cal),
+            "roofline_fc2": add_calibrated(roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2",
+                                                    launches=d["launches"]["fc2"]), cal),
             "grouped_gemm": grouped_gemm_summary(dw, d["touched"], d["per_kernel"]),
             "per_kernel_ms": d["per_kernel"],
+            "step_stats": d["step_stats"],
+            "rows_per_expert": d["histogram"],
         }
         del d
         torch.cuda.empty_cache()
@@ -349,12 +434,15 @@ def main():
                             f"(128x128 block scales), fp8 MFMA, bf16 output",
                 "value": round(rw.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
                 "ms_per_step": round(r["ms"], 4), "dtype": "fp8 e4m3 x e4m3, fp32 accumulate",
-                "roofline": roofline(rw, r["touched"], r["per_kernel"][DOMINANT],
-                                     launches=r["launches"][DOMINANT], fp8_act=True),
-                "roofline_fc2": roofline(rw, r["touched"], r["per_kernel"]["fc2"], "fc2",
-                                         launches=r["launches"]["fc2"], fp8_act=True),
+                "roofline": add_calibrated(roofline(rw, r["touched"], r["per_kernel"][DOMINANT],
+                                                    launches=r["launches"][DOMINANT], fp8_act=True),
+                                           cal, fp8_act=True),
+                "roofline_fc2": add_calibrated(roofline(rw, r["touched"], r["per_kernel"]["fc2"], "fc2",
+                                                        launches=r["launches"]["fc2"], fp8_act=True),
+                                               cal, fp8_act=True),
                 "grouped_gemm": grouped_gemm_summary(rw, r["touched"], r["per_kernel"], fp8_act=True),
                 "per_kernel_ms": r["per_kernel"],
+                "step_stats": r["step_stats"],
             }
             del r
             torch.cuda.empty_cache()
