@@ -993,17 +993,40 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                     if (rr < cur.nrows) store4_bf16(out + (size_t)(cur.row0 + rr) * a.out_ld + col, hv);
                 }
         } else {
+            // FC2: each wave stages its output 16 rows at a time (bf16) in its
+            // share of the ring slot that the next tile fills last, then writes
+            // whole 16-byte column chunks, 2*WTN contiguous bytes per row, instead
+            // of 8-byte pieces scattered over 16 rows per store instruction.  The
+            // region is private to the wave, whose LDS accesses run in order.
+            // Non-temporal stores: fc2_out is read back once, by the finalize.
+            constexpr int PITCH = C::WTN * 2 + 16;  // staged row bytes (+16 spreads the banks)
+            constexpr int CPR = C::WTN / 8;         // 16-byte chunks per row
+            constexpr int RPI = 64 / CPR;           // rows per read / store instruction
+            static_assert(16 * PITCH <= C::STAGE / C::NW && 16 % RPI == 0, "epilogue staging");
+            const int fslot = has_next ? (ring + C::S - 1) % C::S : 0;
+            char* stg = lds + fslot * C::STAGE + wave * (C::STAGE / C::NW);
 #pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
+            for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
                     float v[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
                     quad_transpose(v);
-                    // N is a multiple of 16: a 16-column block is wholly inside or outside
-                    const int col = cur.nt * C::BN + wn * C::WTN + ni * 16 + ecol;
-                    const int rr = cur.m0 + wm * C::WTM + mi * 16 + erow;
-                    if (rr < cur.nrows && col < a.N) store4_bf16(out + (size_t)(cur.row0 + rr) * a.out_ld + col, v);
+                    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<u32x2_t*>(stg + erow * PITCH + (ni * 16 + ecol) * 2) =
+                        u32x2_t{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
                 }
+#pragma unroll
+                for (int j = 0; j < 16 / RPI; ++j) {
+                    const int r = j * RPI + lane / CPR, c = lane % CPR;
+                    const u32x4_t d = *reinterpret_cast<const u32x4_t*>(stg + r * PITCH + c * 16);
+                    const int rr = cur.m0 + wm * C::WTM + mi * 16 + r;
+                    // N is a multiple of 16: a 16-byte chunk is wholly inside or outside
+                    const int col = cur.nt * C::BN + wn * C::WTN + c * 8;
+                    if (rr < cur.nrows && col < a.N)
+                        __builtin_nontemporal_store(d, (__attribute__((address_space(1))) u32x4_t*)(out + (size_t)(cur.row0 + rr) * a.out_ld + col));
+                }
+            }
         }
         // drain: stores and the next tile's first slices; afterwards the stage
         // waits count this block's DMA transfers only
