@@ -1104,13 +1104,12 @@ constexpr int kHandoffMinK = 4096;  // remainder hand-off between classes from t
 // bf16 activations with bf16 or fp8 weights: every row class on the
 // direct-to-LDS engine.
 //
-// A group's last, partial tile goes to the next smaller shape when it is at
-// most one tile of that shape: a big group ending in <= 128 rows past its
-// last full 256-row tile hands them to the mid launch (when the big tiles are
-// 256 rows high), a mid group ending in <= 32 rows past a full 128-row tile
-// to the skinny launch.  The hand-off
-// replaces a mostly-padding tile with one of a quarter / half the MFMA work
-// (the weight tile is read once either way).
+// A big group's last, partial tile goes to the mid launch when it is at most
+// 128 rows (and the big tiles are 256 rows high): a mostly-padding 256-row
+// tile becomes a 128-row one with half the MFMA work (the weight tile is
+// read once either way).  The same hand-off from mid to skinny tiles was
+// measured and is not used: a 32-row tile streams the weights again with a
+// quarter of the waves (fp8 x fp8 Qwen3-shaped FC1 +13%).
 template <int MODE, class Skinny, class Mid, class Big>
 moe_status run_classes_dma(const FfnArgs& f, int R, hipStream_t s, int kid)
 {
@@ -1120,13 +1119,11 @@ moe_status run_classes_dma(const FfnArgs& f, int R, hipStream_t s, int kid)
     // Mixtral-shaped layer (K = 14336) -10%, FC1 of the fp8 x fp8 DeepSeek-V3
     // prefill (K = 7168) -2.5%; with K = 2048 (DeepSeek-V3 FC2) +2.5%.
     const bool handoff = f.K >= kHandoffMinK;
-    const int mid_give = handoff ? Skinny::BM : 0;
     const int big_give = (handoff && Big::BM > Mid::BM) ? Mid::BM : 0;  // none when the shapes match
-    moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid, 0, kMidRows, kBigRows,
-                                               Mid::BM, mid_give);
+    moe_status st = run_dma_gemm<MODE, Skinny>(f, 0, kMidRows, R, s, kid);
     if (st != MOE_OK) return st;
-    st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid, mid_give, kBigRows, kAllRows,
-                                 Big::BM, big_give);
+    st = run_dma_gemm<MODE, Mid>(f, kMidRows, kBigRows, R, s, kid, 0, kBigRows, kAllRows, Big::BM,
+                                 big_give);
     if (st != MOE_OK) return st;
     return run_dma_gemm<MODE, Big>(f, kBigRows, kAllRows, R, s, kid, big_give);
 }

@@ -183,8 +183,8 @@ def test_expert_ffn_empty_groups_and_one_hot():
 
 # group sizes on both sides of every tile-shape and row-class boundary
 # (32/128/256-row tiles; classes [0,64), [64,384), [384,inf)) and of the
-# remainder hand-offs (129, 160, 257: a mid group's last <= 32 rows go to the
-# skinny launch; 513, 640: a big group's last <= 128 rows to the mid launch)
+# remainder hand-off (513, 640: a big group's last <= 128 rows go to the mid
+# launch; 641 keeps its 129-row remainder)
 CLASS_EDGE_ROWS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 161, 255, 256, 257, 383, 384, 385, 511,
                    512, 513, 640, 641]
 
