@@ -42,9 +42,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(text=None):
+    """Hash of the GEMM source with comments and whitespace removed, so that the
+    traffic summaries stay valid across comment-only edits."""
+    import re
+    if text is None:
+        with open(KERNEL_SOURCE) as f:
+            text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def fc_work(w, touched_groups, which, fp8_act=False):

@@ -439,18 +439,20 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Tile engine with direct global->LDS loads (bf16 activations; bf16 or fp8
-// weights).
+// Tile engine with direct global->LDS loads (bf16 activations with bf16 or
+// fp8 weights; fp8 activations with fp8 weights).
 //
-// Each stage is one K slice of 64 values: BM activation rows of 128 bytes and
-// BN weight rows of 128 bytes (bf16) or 64 bytes (fp8), written straight into
-// LDS by global_load_lds_dwordx4: one instruction moves 1 KB, lane l landing
-// at byte 16*l, i.e. 8 activation rows or 8 bf16 / 16 fp8 weight rows, every
-// lane request a full line or half line.  A ring of S stages keeps S-1 slices
-// in flight without holding anything in VGPRs; one LDS-only barrier per
-// slice.  The next tile's token indices are fetched when a tile starts and its
-// first slices are issued before the current tile's epilogue, so a tile change
-// exposes only the epilogue's store drain.
+// Each stage is one K slice: BM activation rows of 128 bytes (64 bf16 or 128
+// fp8 values) and BN weight rows of 128 bytes, or 64 bytes for fp8 weights
+// under bf16 activations, written straight into LDS by
+// global_load_lds_dwordx4: one instruction moves 1 KB, lane l landing at byte
+// 16*l, i.e. 8 rows of 128 bytes or 16 of 64, every lane request a full line
+// or half line.  Sources are a scalar base (activations, the tile's expert
+// weights, activation scales) plus a 32-bit per-lane offset.  A ring of S
+// stages keeps S-1 slices in flight without holding anything in VGPRs; one
+// LDS-only barrier per slice.  The next tile's token indices are fetched when
+// a tile starts and its first slices are issued before the current tile's
+// epilogue, so a tile change exposes only the epilogue.
 //
 // fp8 weights (W8): a lane reads its 8 fp8 values of a fragment from LDS and
 // widens them to bf16 (exact: every e4m3 value is a bf16 value); the MFMA
@@ -460,12 +462,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(FfnArgs a)
 //
 // fp8 activations (A8, with fp8 weights): a stage is one 128-wide K block,
 // 128-byte rows of fp8 codes for both operands, multiplied on
-// v_mfma_f32_16x16x128_f8f6f4 (exact products, fp32 sums).  Each wave also
-// stages the 1x128 activation scales of its own WTM rows for that block (one
+// v_mfma_f32_16x16x128_f8f6f4 (exact products; the instruction's own sum of
+// 128 products is not exactly rounded fp32, ~13 bits measured, hence one
+// MFMA per block and fp32 accumulation across blocks).  Each wave also stages
+// the 1x128 activation scales of its own WTM rows for that block (one
 // 4-byte-per-lane transfer into a private 256-byte slot), and adds each
 // block's MFMA result to the accumulator times (row scale x weight-block
-// scale).  FC1's epilogue quantises h per row and 128 intermediate channels
-// (one 256-column tile holds exactly one such block of every row).
+// scale), software-pipelined one MFMA behind.  FC1's epilogue quantises h per
+// row and 128 intermediate channels (one 256-column tile holds exactly one
+// such block of every row).
 template <int BM_, int BN_, int WM_, int WN_, int GM_, int S_, bool W8_ = false, bool A8_ = false>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, GM = GM_, S = S_;
