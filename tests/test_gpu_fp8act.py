@@ -343,3 +343,14 @@ def test_layer_fp8act_graph_capture_replays():
     toks = np.arange(0, w.T, 7, dtype=np.int32)
     ref = oracle.layer_tokens(W, qo, "fp8", w.T, w.k, w.E, 1, ids, sc, toks, x_scale=so)
     assert rel_l2(host(y_graph).double().numpy()[toks], ref) < TOL
+
+
+@pytest.mark.parametrize("T,H,I,E,k,n_shared", [(1, 128, 128, 1, 1, 0), (3, 256, 128, 4, 4, 2),
+                                                (17, 384, 640, 5, 2, 1)])
+def test_expert_ffn_fp8_degenerate_shapes(T, H, I, E, k, n_shared):
+    """One token and one expert; k = E with two shared experts; H and I that
+    leave partial 256-wide N tiles in both GEMMs."""
+    w = fp8_workload(T, H, I, E, k, n_shared=n_shared, method=4)
+    err, got, ref = run_ffn_fp8_check(w, wl.make_inputs(w, 5))
+    row_err = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err < TOL and row_err.max() < ROW_TOL, (err, row_err.max())
