@@ -405,3 +405,39 @@ def test_kernel_timing_hooks():
     # each grouped GEMM is one launch per row class (same count every call)
     for name in ("fc1", "fc2"):
         assert t[name][1] >= 3 and t[name][1] % 3 == 0 and t[name][0] > 0, (name, t[name])
+
+
+def test_shared_expert_as_separate_call_on_second_stream():
+    """The shared expert run as its own expert_ffn call (one group over all
+    tokens, identity rows, writing fc2_out rows P..P+T) on a second stream,
+    concurrent with route / permute / the routed FFN, gives the one-call
+    layer's output bit for bit."""
+    w = small_workload("bf16", "bf16", T=600, E=16, k=4, n_shared=1, method=2, n_group=4,
+                       topk_group=2, scaling=2.5, bias=True)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in wl.make_inputs(w, 9).items()}
+    layer = moe.layer_for_workload(w, DEV)
+    y_one = layer(g["x"], g["logits"], g["w13"], g["w2"], g["bias"], None, None).clone()
+    T, k, E, H, I, P = w.T, w.k, w.E, w.H, w.I, w.P
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    sc = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pp = torch.empty(P, dtype=torch.int32, device=DEV)
+    up = torch.empty(P, dtype=torch.int32, device=DEV)
+    fc2 = torch.full((P + T, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws_r = moe.alloc_workspace(T, k, E, 0, H, I, torch.bfloat16, DEV)
+    ws_s = moe.alloc_workspace(T, 1, 1, 0, H, I, torch.bfloat16, DEV)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        moe.expert_ffn(g["x"], torch.tensor([0, T], dtype=torch.int32, device=DEV),
+                       torch.arange(T, dtype=torch.int32, device=DEV), g["w13"][E:E + 1],
+                       g["w2"][E:E + 1], 1, 1, 0, ws=ws_s, out=fc2[P:])
+    moe.route(g["logits"], k, w.method, w.n_group, w.topk_group, g["bias"], w.scaling, False,
+              out=(ids, sc))
+    moe.permute(ids, E, 0, ws=ws_r, out=(off, pp, up))
+    moe.expert_ffn(g["x"], off, pp, g["w13"][:E], g["w2"][:E], k, E, 0, ws=ws_r, out=fc2[:P])
+    main.wait_stream(side)
+    y_split = moe.finalize(fc2, up, sc, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y_split.view(torch.int16), y_one.view(torch.int16))
