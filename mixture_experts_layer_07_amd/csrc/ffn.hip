@@ -159,8 +159,8 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4])
 // Four consecutive bf16 outputs (8 bytes, 8-byte aligned)
 __device__ __forceinline__ void store4_bf16(bf16_t* p, const float (&v)[4])
 {
-    const unsigned lo = (unsigned)f32_to_bf16(v[0]) | ((unsigned)f32_to_bf16(v[1]) << 16);
-    const unsigned hi = (unsigned)f32_to_bf16(v[2]) | ((unsigned)f32_to_bf16(v[3]) << 16);
+    const unsigned lo = pack_bf16x2(v[0], v[1]);
+    const unsigned hi = pack_bf16x2(v[2], v[3]);
     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
     *(__attribute__((address_space(1))) u32x2_t*)(p) = u32x2_t{lo, hi};
 }
@@ -1018,8 +1018,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                     quad_transpose(v);
                     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
                     *reinterpret_cast<u32x2_t*>(stg + erow * PITCH + (ni * 16 + ecol) * 2) =
-                        u32x2_t{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                                (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+                        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                 }
 #pragma unroll
                 for (int j = 0; j < 16 / RPI; ++j) {
