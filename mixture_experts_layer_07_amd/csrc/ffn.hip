@@ -116,6 +116,9 @@ struct Cfg {
     static_assert(sizeof(AT) == sizeof(WT) && sizeof(WT) >= 2, "fp32 or bf16 operands");
 };
 
+// One 16x16 result block from a 16-row fragment pair (K-contiguous rows of
+// each operand): lane l gets rows 4*(l/16) + i (i < 4) of column l%16, rows
+// indexing the first operand's fragment and columns the second's.
 __device__ __forceinline__ f32x4_t mfma_frag(u32x4_t a, u32x4_t b, f32x4_t c, bf16_t)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -133,28 +136,6 @@ __device__ __forceinline__ f32x4_t mfma_frag(u32x4_t a, u32x4_t b, f32x4_t c, fl
 
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t* p, float v) { *p = f32_to_bf16(v); }
-
-// 4x4 transpose across the four lanes of a quad (lanes 4k .. 4k+3): on entry
-// quad lane t holds v[i] = M[i][t], on exit v[i] = M[t][i].  Two butterfly
-// stages over DPP quad permutations; a register moves in a stage when its
-// index and the lane differ in that stage's bit.
-__device__ __forceinline__ void quad_transpose(float (&v)[4])
-{
-    const int t = threadIdx.x & 3;
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)  // from lane t^1: quad_perm [1,0,3,2]
-        x[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i ^ 1]), 0xB1, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if ((i ^ t) & 1) v[i] = x[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)  // from lane t^2: quad_perm [2,3,0,1]
-        x[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i ^ 2]), 0x4E, 0xF, 0xF, false));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if ((i ^ t) & 2) v[i] = x[i];
-}
 
 // Four consecutive bf16 outputs (8 bytes, 8-byte aligned)
 __device__ __forceinline__ void store4_bf16(bf16_t* p, const float (&v)[4])
@@ -805,28 +786,21 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 }
                 const float* lsa = reinterpret_cast<const float*>(lb + C::B_BYTES + wave * 256);
                 const int g4 = lane >> 4;
-                f32x4_t sa[C::MI];
+                // the result rows of lane l are activation row l % 16 of each
+                // 16-row block (operands swapped, see mfma_frag): one row scale
+                // per lane and block, times the gate / up (FC1) or the single
+                // (FC2) weight-block scale of the wave's columns
+                float s0[C::MI], s1[C::MI];
                 i32x8_t fa[C::MI];
 #pragma unroll
                 for (int mi = 0; mi < C::MI; ++mi) {
-                    sa[mi] = *reinterpret_cast<const f32x4_t*>(lsa + mi * 16 + g4 * 4);
+                    const float sa = lsa[mi * 16 + (lane & 15)];
+                    s0[mi] = sa * sw0;
+                    s1[mi] = sa * sw1;
                     fa[mi] = lds_row32(la, wm * C::WTM + mi * 16 + (lane & 15), g4);
                 }
                 // Software pipeline: the VALU that scales MFMA result j runs
-                // after MFMA j+2 has been issued, so it does not wait for j.
-                // scale products per slice where the registers allow: FC2 has one
-                // weight block per wave (sa becomes sa * sw); FC1 two (gate, up),
-                // precomputed for 64x64 wave tiles, applied per MFMA otherwise
-                constexpr bool PRE1 = C::MI * C::NI <= 16;
-                f32x4_t su[PRE1 ? C::MI : 1];
-                if (MODE == FC1 && PRE1) {
-#pragma unroll
-                    for (int mi = 0; mi < C::MI; ++mi) su[mi] = sa[mi] * sw1;
-                }
-                if (MODE == FC2 || PRE1) {
-#pragma unroll
-                    for (int mi = 0; mi < C::MI; ++mi) sa[mi] *= sw0;
-                }
+                // after MFMA j+1 has been issued, so it does not wait for j.
                 constexpr int NB = C::MI * C::NI, LAGB = 2;
                 f32x4_t pr[LAGB + 1];
                 i32x8_t fb[2];
@@ -837,16 +811,11 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                         const int mi = j % C::MI, ni = j / C::MI;
                         if (mi == 0 && ni + 1 < C::NI)
                             fb[(ni + 1) & 1] = lds_row32(lb, wn * C::WTN + (ni + 1) * 16 + (lane & 15), g4);
-                        pr[j % (LAGB + 1)] = mfma_fp8(fa[mi], fb[ni & 1]);
+                        pr[j % (LAGB + 1)] = mfma_fp8(fb[ni & 1], fa[mi]);
                     }
                     if (j >= LAGB) {
                         const int jj = j - LAGB, mi = jj % C::MI, ni = jj / C::MI;
-                        if (MODE == FC2)
-                            acc[mi][ni] += sa[mi] * pr[jj % (LAGB + 1)];
-                        else if constexpr (PRE1)
-                            acc[mi][ni] += ((ni & 1) ? su[mi % (PRE1 ? C::MI : 1)] : sa[mi]) * pr[jj % (LAGB + 1)];
-                        else
-                            acc[mi][ni] += sa[mi] * (((ni & 1) ? sw1 : sw0) * pr[jj % (LAGB + 1)]);
+                        acc[mi][ni] += ((MODE == FC1 && (ni & 1)) ? s1[mi] : s0[mi]) * pr[jj % (LAGB + 1)];
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -876,8 +845,8 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < C::NI; ++ni) {
-                        if constexpr (C::WNARROW) part[mi][ni] = mfma_frag(fa[mi], fb[ni], part[mi][ni], bf16_t());
-                        else acc[mi][ni] = mfma_frag(fa[mi], fb[ni], acc[mi][ni], bf16_t());
+                        if constexpr (C::WNARROW) part[mi][ni] = mfma_frag(fb[ni], fa[mi], part[mi][ni], bf16_t());
+                        else acc[mi][ni] = mfma_frag(fb[ni], fa[mi], acc[mi][ni], bf16_t());
                     }
             }
             }
@@ -924,16 +893,17 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                 if (st < nk) issue((ring + st) % C::S, st);
         }
 
-        // Epilogue.  An MFMA block leaves lane l with rows 4*(l/16) + i (i < 4)
-        // of column l%16; a quad transpose gives each lane one row and four
-        // consecutive columns (4*((l%16)/4) + i), stored as one 8-byte write.
+        // Epilogue.  With the weight fragment as the MFMA's first operand, a
+        // 16x16 result block leaves lane l the activation row l%16 and the four
+        // consecutive output columns 4*(l/16) + i (i < 4): one 8-byte bf16 write
+        // (or a 4-byte fp8 one) per lane and block, no data exchange.
         bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
-        const int erow = (lane >> 4) * 4 + (lane & 3);  // row within a 16x16 block
-        const int ecol = lane & 12;                      // first of its 4 columns
+        const int erow = lane & 15;        // row within a 16x16 block
+        const int ecol = (lane >> 4) * 4;  // first of its 4 columns
         if (MODE == FC1 && C::A8) {
             // h -> e4m3 per row and 128 intermediate channels: the tile's 128 h
-            // columns are split over the WN wave columns, 4 lanes per row each.
-            // h (quad-transposed) overwrites the gate accumulators.
+            // columns are split over the WN wave columns, 4 lanes per row each
+            // (lanes l, l^16, l^32, l^48).  h overwrites the gate accumulators.
             float rmax[C::MI];
 #pragma unroll
             for (int mi = 0; mi < C::MI; ++mi) {
@@ -947,16 +917,15 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                         const float up = acc[mi][2 * q + 1][i];
                         hv[i] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
                     }
-                    quad_transpose(hv);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         acc[mi][2 * q][i] = hv[i];
                         rmax[mi] = fmaxf(rmax[mi], fabsf(hv[i]));
                     }
                 }
-                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 4, 64));
-                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 8, 64));
-                if (((lane >> 2) & 3) == 0) s_amax[(wm * C::WTM + mi * 16 + erow) * C::WN + wn] = rmax[mi];
+                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 16, 64));
+                rmax[mi] = fmaxf(rmax[mi], __shfl_xor(rmax[mi], 32, 64));
+                if (lane < 16) s_amax[(wm * C::WTM + mi * 16 + erow) * C::WN + wn] = rmax[mi];
             }
             lds_barrier();
             uint8_t* hq = reinterpret_cast<uint8_t*>(a.out);
@@ -976,7 +945,7 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                         const int col = cur.nt * (C::BN / 2) + ((wn * C::WTN) / 32 + q) * 16 + ecol;
                         *(__attribute__((address_space(1))) uint32_t*)(hq + r * a.I + col) = fp8x4_code(hv, sc);
                     }
-                    if (wn == 0 && ((lane >> 2) & 3) == 0) a.out_scale[r * sk_out + cur.nt] = sc;
+                    if (wn == 0 && lane < 16) a.out_scale[r * sk_out + cur.nt] = sc;
                 }
             }
         } else if (MODE == FC1) {
@@ -991,7 +960,6 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
                         const float up = acc[mi][2 * q + 1][i];
                         hv[i] = gt * __builtin_amdgcn_rcpf(1.0f + expf(-gt)) * up;
                     }
-                    quad_transpose(hv);
                     const int pair = (wn * C::WTN) / 32 + q;
                     const int col = cur.nt * (C::BN / 2) + pair * 16 + ecol;
                     const int rr = cur.m0 + wm * C::WTM + mi * 16 + erow;
@@ -1014,11 +982,9 @@ __global__ __launch_bounds__(C::NT) void dma_gemm_kernel(FfnArgs a)
             for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
                 for (int ni = 0; ni < C::NI; ++ni) {
-                    float v[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
-                    quad_transpose(v);
                     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
                     *reinterpret_cast<u32x2_t*>(stg + erow * PITCH + (ni * 16 + ecol) * 2) =
-                        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        u32x2_t{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
                 }
 #pragma unroll
                 for (int j = 0; j < 16 / RPI; ++j) {
