@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"hbm": 8000.0, "bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # GB/s, TFLOP/s
 DOMINANT = "fc1"
-KERNEL_SOURCE = os.path.join(ROOT, "mixture_experts_layer_07_amd", "csrc", "ffn.hip")
+# sources of the grouped GEMM kernels (the tile engine's helpers live in dma.h)
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_07_amd", "csrc", f)
+                  for f in ("ffn.hip", "dma.h")]
 
 
 def log(*a):
@@ -43,12 +45,14 @@ def log(*a):
 
 
 def kernel_sha(text=None):
-    """Hash of the GEMM source with comments and whitespace removed, so that the
+    """Hash of the GEMM sources with comments and whitespace removed, so that the
     traffic summaries stay valid across comment-only edits."""
     import re
     if text is None:
-        with open(KERNEL_SOURCE) as f:
-            text = f.read()
+        text = ""
+        for p in KERNEL_SOURCES:
+            with open(p) as f:
+                text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
