@@ -108,6 +108,31 @@ def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=Non
             "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
 
 
+def fused_summary(w, touched, res, two_call_kernels, fp8_act=False):
+    """The fused FC1+FC2 kernel (h kept on chip) on the same inputs: its time
+    per step beside FC1 + FC2 of the two-call path, and its roofline.  Its
+    algorithmic bytes are those of both GEMMs minus the h round trip."""
+    f1, b1 = fc_work(w, touched, "fc1", fp8_act)
+    f2, b2 = fc_work(w, touched, "fc2", fp8_act)
+    qsz = 1 + 4.0 / 128 if fp8_act else 2
+    flops, nbytes = f1 + f2, b1 + b2 - 2 * w.R * w.I * qsz
+    ms = res["per_kernel"]["ffn_fused"]
+    s = ms * 1e-3
+    peak_f = mfma_peak(w, fp8_act)
+    if flops / (peak_f * 1e12) >= nbytes / (PEAK["hbm"] * 1e9):
+        ach, peak, unit, bound = flops / s / 1e12, peak_f, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = nbytes / s / 1e9, PEAK["hbm"], "GB/s", "hbm"
+    two = two_call_kernels["fc1"] + two_call_kernels["fc2"]
+    return {"kernel": "fused FC1+SwiGLU+FC2, h in LDS (one launch per step)",
+            "layer_ms_per_step": round(res["ms"], 4), "ffn_ms_per_step": round(ms, 4),
+            "two_call_ffn_ms_per_step": round(two, 4), "ffn_speedup_vs_two_call": round(two / ms, 3),
+            "split": res["split"],
+            "roofline": {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4), "traffic": None,
+                         "algorithmic_bytes": nbytes, "algorithmic_flops": flops}}
+
+
 def grouped_gemm_summary(w, touched, per_kernel, fp8_act=False):
     """FC1 + FC2 together: the layer's expert-FFN FLOPs (real rows, not padded
     tiles) and algorithmic bytes over the two GEMMs' time per step."""
@@ -246,7 +271,35 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
     print(json.dumps(out, indent=1))
 
 
-def run_workload(name, steps, warmup, device, fp8_act=False):
+def time_layer(layer, inp, steps, warmup):
+    """ms per step of layer(inp) and its per-kernel ms per step (HIP-event hooks
+    on, in a second pass of as many steps)."""
+    import torch
+    import mixture_experts_layer_07_amd as moe
+
+    def step():
+        return layer(inp["x"], inp["logits"], inp["w13"], inp["w2"], inp["bias"],
+                     inp["w13_scale"], inp["w2_scale"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    moe.timing_enable(True)
+    moe.kernel_times(reset=True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kt = moe.kernel_times(reset=True)
+    moe.timing_enable(False)
+    return ms, {k: round(v[0] / steps, 4) for k, v in kt.items()}
+
+
+def run_workload(name, steps, warmup, device, fp8_act=False, fused=False):
     import torch
     import mixture_experts_layer_07_amd as moe
     from mixture_experts_layer_07_amd import workloads as wl
@@ -296,7 +349,14 @@ def run_workload(name, steps, warmup, device, fp8_act=False):
     log(f"[bench] {name}: {ms:.3f} ms/step, per-kernel ms per step {per_kernel}, launches per step {launches}")
     log(f"[bench] {name}: rows per expert min {int(cnt.min())} median "
         f"{int(cnt.median())} max {int(cnt.max())}, empty experts {int((cnt == 0).sum())}")
-    return dict(w=w, inp=inp, layer=layer, ms=ms, per_kernel=per_kernel, touched=touched,
+    fres = None
+    if fused and w.act == "bf16" and w.I <= moe.binding.FUSED_MAX_I:
+        lf = moe.layer_for_workload(w, device, fp8_act=fp8_act, fused=True)
+        fms, fk = time_layer(lf, inp, steps, warmup)
+        fres = dict(ms=fms, per_kernel=fk, split="automatic")
+        log(f"[bench] {name} fused FFN: {fms:.3f} ms/step, per-kernel ms per step {fk}")
+        del lf
+    return dict(w=w, inp=inp, layer=layer, ms=ms, per_kernel=per_kernel, touched=touched, fused=fres,
                 counts=cnt, launches=launches,
                 step_stats={"median_ms": round(step_ms[len(step_ms) // 2], 4),
                             "min_ms": round(step_ms[0], 4),
@@ -351,6 +411,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--fp8act-workloads", nargs="*", default=["dsv3_prefill_fp8", "dsv3_decode_fp8"],
                     help="workloads also run on the fp8-activation path (none: skip)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip timing the fused FC1+FC2 kernel beside each workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
@@ -380,7 +442,8 @@ def main():
     cal = None if args.no_calibration else calibrate(dev)
     if cal:
         log(f"[bench] calibration {cal}")
-    main_res = run_workload(args.workload, args.steps, args.warmup, dev)
+    fz = not args.no_fused
+    main_res = run_workload(args.workload, args.steps, args.warmup, dev, fused=fz)
     w = main_res["w"]
     traffic = load_traffic(args.workload)
     rl = roofline(w, main_res["touched"], main_res["per_kernel"][DOMINANT], traffic=traffic,
@@ -411,13 +474,15 @@ def main():
         "rows_per_expert": main_res["histogram"],
         "calibration": cal,
     }
+    if main_res["fused"]:
+        out["fused_ffn"] = fused_summary(w, main_res["touched"], main_res["fused"], main_res["per_kernel"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']}")
     del main_res
     torch.cuda.empty_cache()
     if not args.no_decode:
-        d = run_workload(args.decode_workload, args.steps, args.warmup, dev)
+        d = run_workload(args.decode_workload, args.steps, args.warmup, dev, fused=fz)
         dw = d["w"]
         out["decode"] = {
             "workload": f"{dw.name}: T={dw.T} H={dw.H} E={dw.E} I={dw.I} top-{dw.k}",
@@ -433,12 +498,14 @@ def main():
             "step_stats": d["step_stats"],
             "rows_per_expert": d["histogram"],
         }
+        if d["fused"]:
+            out["decode"]["fused_ffn"] = fused_summary(dw, d["touched"], d["fused"], d["per_kernel"])
         del d
         torch.cuda.empty_cache()
     if args.fp8act_workloads:
         out["fp8_activations"] = {}
         for name in args.fp8act_workloads:
-            r = run_workload(name, args.steps, args.warmup, dev, fp8_act=True)
+            r = run_workload(name, args.steps, args.warmup, dev, fp8_act=True, fused=fz)
             rw = r["w"]
             out["fp8_activations"][name] = {
                 "workload": f"{rw.name}: T={rw.T} H={rw.H} E={rw.E}+{rw.n_shared} shared I={rw.I} "
@@ -456,6 +523,9 @@ def main():
                 "per_kernel_ms": r["per_kernel"],
                 "step_stats": r["step_stats"],
             }
+            if r["fused"]:
+                out["fp8_activations"][name]["fused_ffn"] = fused_summary(
+                    rw, r["touched"], r["fused"], r["per_kernel"], fp8_act=True)
             del r
             torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)

@@ -13,7 +13,9 @@
  *   moe_finalize   weighted gather-sum of each token's k FFN rows (+ shared)
  *
  * With fp8 activations the FFN step is moe_quantize_fp8 (of x) followed by
- * moe_expert_ffn_fp8; route, permute and finalize are unchanged.
+ * moe_expert_ffn_fp8; route, permute and finalize are unchanged.  The FFN step
+ * can also run as one kernel that keeps h on chip (moe_expert_ffn_fused,
+ * moe_expert_ffn_fp8_fused; same results, no workspace).
  *
  * Conventions shared by every call:
  *  - Pointers named as device buffers are device pointers (hipMalloc'd or
@@ -79,6 +81,9 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype
  * 32-expert group-size limit does not apply here: groups go through LDS). */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
+/* Largest intermediate size of the fused FC1+FC2 kernels (h of a 16-row tile
+ * is kept in LDS). */
+#define MOE_FUSED_MAX_I 2048
 
 /*
  * moe_route -- per-token expert selection and weights.
@@ -238,6 +243,47 @@ moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, in
                               const float* w13_scale, const float* w2_scale, void* fc2_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_expert_ffn_fused -- moe_expert_ffn as ONE kernel that keeps h on chip:
+ * FC1 and FC2 fused, the intermediate never written to memory (the FC12 form
+ * of the TensorRT-LLM page, section "MoE 后端:同一个接口,多种实现").  A
+ * workgroup takes 16 rows of one group, computes their h [16, I] into LDS
+ * (FC1 + SwiGLU over all I channels), then their FC2 rows from it.
+ * Results are bit-identical to moe_expert_ffn for the same arguments.
+ *
+ *  act        MOE_BF16 (MOE_F32 is MOE_ERR_UNSUPPORTED).
+ *  wdt        MOE_BF16 or MOE_FP8_E4M3 (with w13_scale, w2_scale).
+ *  I          at most MOE_FUSED_MAX_I (h of 16 rows fills the LDS);
+ *             larger I is MOE_ERR_UNSUPPORTED.
+ *  split      workgroups that share one 16-row tile: each computes the tile's
+ *             h (FC1 repeated) and takes every split-th 128- or 256-column
+ *             block of its FC2.  0 picks it from the shape (about two work
+ *             items per CU); values above the number of FC2 column blocks are
+ *             clamped to it; negative values and values above 64 are
+ *             MOE_ERR_INVALID_ARG.  Results do not depend on it.
+ *  other arguments as for moe_expert_ffn; there is no workspace.
+ * Limits: x and one expert's w13 below 4 GiB.
+ */
+moe_status moe_expert_ffn_fused(const void* x, int act, int T, int H, int I, int k, int E,
+                                int n_shared, const int32_t* expert_offsets,
+                                const int32_t* permuted_pair, const void* w13, const void* w2,
+                                int wdt, const float* w13_scale, const float* w2_scale, int split,
+                                void* fc2_out, void* stream);
+
+/*
+ * moe_expert_ffn_fp8_fused -- moe_expert_ffn_fp8 as one kernel with h on chip:
+ * the e4m3 codes of h and their per-row, per-128-channel scales (quantised as
+ * moe_expert_ffn_fp8 quantises them) stay in LDS between FC1 and FC2.
+ * Results are bit-identical to moe_expert_ffn_fp8.  I <= MOE_FUSED_MAX_I;
+ * split as for moe_expert_ffn_fused; no workspace; other arguments as for
+ * moe_expert_ffn_fp8.
+ */
+moe_status moe_expert_ffn_fp8_fused(const uint8_t* xq, const float* x_scale, int T, int H, int I,
+                                    int k, int E, int n_shared, const int32_t* expert_offsets,
+                                    const int32_t* permuted_pair, const uint8_t* w13,
+                                    const uint8_t* w2, const float* w13_scale,
+                                    const float* w2_scale, int split, void* fc2_out, void* stream);
+
 /* Bytes of workspace that moe_permute and moe_expert_ffn need for this shape
  * (0 on invalid arguments).  One buffer of this size serves both calls.
  * act = MOE_FP8_E4M3 sizes it for moe_expert_ffn_fp8. */
@@ -264,7 +310,8 @@ enum {
     MOE_KID_FC2 = 5,
     MOE_KID_FINALIZE = 6,
     MOE_KID_QUANT = 7,
-    MOE_NUM_KIDS = 8
+    MOE_KID_FFN_FUSED = 8,
+    MOE_NUM_KIDS = 9
 };
 moe_status moe_timing_enable(int enable);
 moe_status moe_kernel_times(double* ms /*[MOE_NUM_KIDS]*/, int64_t* launches /*[MOE_NUM_KIDS]*/,

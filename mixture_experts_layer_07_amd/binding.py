@@ -21,7 +21,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 ROUTE_DEFAULT, ROUTE_RENORMALIZE, ROUTE_DEEPSEEKV3, ROUTE_RENORMALIZE_NAIVE = 0, 1, 2, 4
 ROUTE_FLAG_RENORMALIZE = 1
 KERNEL_IDS = ["route", "permute_count", "permute_scan", "permute_scatter", "fc1", "fc2",
-              "finalize", "quantize"]
+              "finalize", "quantize", "ffn_fused"]
+FUSED_MAX_I = 2048
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 _lib = None
@@ -48,6 +49,8 @@ def lib():
         L.moe_finalize.argtypes = [P, i, P, P, i, i, i, i, P, i, P]
         L.moe_quantize_fp8.argtypes = [P, i, i, i, P, P, P]
         L.moe_expert_ffn_fp8.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P, P, P, P, z, P]
+        L.moe_expert_ffn_fused.argtypes = [P, i, i, i, i, i, i, i, P, P, P, P, i, P, P, i, P, P]
+        L.moe_expert_ffn_fp8_fused.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P]
         L.moe_workspace_size.argtypes = [i, i, i, i, i, i, i]
         L.moe_workspace_size.restype = z
         L.moe_status_string.argtypes = [i]
@@ -57,7 +60,8 @@ def lib():
         L.moe_timing_enable.argtypes = [i]
         L.moe_kernel_times.argtypes = [P, P, i]
         for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_finalize",
-                   "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_timing_enable",
+                   "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_expert_ffn_fused",
+                   "moe_expert_ffn_fp8_fused", "moe_timing_enable",
                    "moe_kernel_times"):
             getattr(L, fn).restype = C.c_int
         _lib = L
@@ -225,6 +229,62 @@ def expert_ffn_fp8(xq, x_scale, expert_offsets, permuted_pair, w13, w2, w13_scal
         _ptr(xq), _ptr(x_scale), T, H, I, k, E, n_shared, _ptr(expert_offsets),
         _ptr(permuted_pair), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale), _ptr(out),
         _ptr(ws), ws.numel(), _stream(xq.device)))
+    return out
+
+
+def expert_ffn_fused(x, expert_offsets, permuted_pair, w13, w2, k, E, n_shared=0, w13_scale=None,
+                     w2_scale=None, split=0, out=None):
+    """moe_expert_ffn_fused (one kernel, h kept on chip) -> fc2_out bf16
+    [T*k + n_shared*T, H]; same results as expert_ffn, no workspace."""
+    _dev(x, "x", torch.bfloat16)
+    T, H = x.shape
+    G = E + n_shared
+    _dev(w13, "w13", (torch.bfloat16, torch.float8_e4m3fn))
+    I = w13.shape[1] // 2
+    _dev(w13, "w13", shape=(G, 2 * I, H))
+    _dev(w2, "w2", w13.dtype, (G, H, I))
+    _dev(expert_offsets, "expert_offsets", torch.int32, (G + 1,))
+    _dev(permuted_pair, "permuted_pair", torch.int32, (T * k,))
+    if w13.dtype == torch.float8_e4m3fn:
+        _dev(w13_scale, "w13_scale", torch.float32, (G, 2 * I // 128, H // 128))
+        _dev(w2_scale, "w2_scale", torch.float32, (G, H // 128, I // 128))
+    R = T * k + n_shared * T
+    if out is None:
+        out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "fc2_out", torch.bfloat16, (R, H))
+    _check("moe_expert_ffn_fused", lib().moe_expert_ffn_fused(
+        _ptr(x), BF16, T, H, I, k, E, n_shared, _ptr(expert_offsets), _ptr(permuted_pair),
+        _ptr(w13), _ptr(w2), _DT[w13.dtype], _ptr(w13_scale), _ptr(w2_scale), int(split),
+        _ptr(out), _stream(x.device)))
+    return out
+
+
+def expert_ffn_fp8_fused(xq, x_scale, expert_offsets, permuted_pair, w13, w2, w13_scale, w2_scale,
+                         k, E, n_shared=0, split=0, out=None):
+    """moe_expert_ffn_fp8_fused -> fc2_out bf16 [T*k + n_shared*T, H]; same results as
+    expert_ffn_fp8, no workspace."""
+    _dev(xq, "xq", torch.float8_e4m3fn)
+    T, H = xq.shape
+    _dev(x_scale, "x_scale", torch.float32, (T, H // 128))
+    G = E + n_shared
+    _dev(w13, "w13", torch.float8_e4m3fn)
+    I = w13.shape[1] // 2
+    _dev(w13, "w13", shape=(G, 2 * I, H))
+    _dev(w2, "w2", torch.float8_e4m3fn, (G, H, I))
+    _dev(w13_scale, "w13_scale", torch.float32, (G, 2 * I // 128, H // 128))
+    _dev(w2_scale, "w2_scale", torch.float32, (G, H // 128, I // 128))
+    _dev(expert_offsets, "expert_offsets", torch.int32, (G + 1,))
+    _dev(permuted_pair, "permuted_pair", torch.int32, (T * k,))
+    R = T * k + n_shared * T
+    if out is None:
+        out = torch.empty((R, H), dtype=torch.bfloat16, device=xq.device)
+    else:
+        _dev(out, "fc2_out", torch.bfloat16, (R, H))
+    _check("moe_expert_ffn_fp8_fused", lib().moe_expert_ffn_fp8_fused(
+        _ptr(xq), _ptr(x_scale), T, H, I, k, E, n_shared, _ptr(expert_offsets),
+        _ptr(permuted_pair), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale), int(split),
+        _ptr(out), _stream(xq.device)))
     return out
 
 

@@ -10,7 +10,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "finalize.hip", "quant.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "fused.hip", "finalize.hip",
+           "quant.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

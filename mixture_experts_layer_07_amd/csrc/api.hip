@@ -281,6 +281,69 @@ moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, in
                           w13_scale, w2_scale, fc2_out, ws, static_cast<hipStream_t>(stream));
 }
 
+// Checks shared by the two fused entry points (act: MOE_BF16 or, for the
+// fp8 x fp8 form, MOE_FP8_E4M3).
+static moe_status check_fused(int T, int H, int I, int k, int E, int n_shared, int act, int wdt,
+                              int split)
+{
+    moe_status st = check_common(T, k, E, n_shared);
+    if (st != MOE_OK) return st;
+    if (H < 1 || I < 1) return set_error(MOE_ERR_INVALID_ARG, "H and I must be positive (H=%d, I=%d)", H, I);
+    if (H % 128 || I % 128)
+        return set_error(MOE_ERR_UNSUPPORTED, "H and I must be multiples of 128 (H=%d, I=%d)", H, I);
+    if (I > MOE_FUSED_MAX_I)
+        return set_error(MOE_ERR_UNSUPPORTED, "I = %d exceeds the fused kernel's limit %d (h is kept in LDS)",
+                         I, MOE_FUSED_MAX_I);
+    if (split < 0 || split > 64) return set_error(MOE_ERR_INVALID_ARG, "split must be in [0, 64] (got %d)", split);
+    const unsigned long long lim = 1ull << 32;
+    const int asz = act == MOE_FP8_E4M3 ? 1 : 2, wsz = wdt == MOE_FP8_E4M3 ? 1 : 2;
+    if ((unsigned long long)T * H * asz >= lim || 2ull * I * H * wsz >= lim)
+        return set_error(MOE_ERR_UNSUPPORTED, "x or one expert's weights exceed 4 GiB (T=%d, H=%d, I=%d)", T, H, I);
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_fused(const void* x, int act, int T, int H, int I, int k, int E,
+                                int n_shared, const int32_t* expert_offsets,
+                                const int32_t* permuted_pair, const void* w13, const void* w2,
+                                int wdt, const float* w13_scale, const float* w2_scale, int split,
+                                void* fc2_out, void* stream)
+{
+    if (act == MOE_F32) return set_error(MOE_ERR_UNSUPPORTED, "the fused kernel takes bf16 activations");
+    if (act != MOE_BF16) return set_error(MOE_ERR_INVALID_ARG, "activation dtype %d must be MOE_BF16", act);
+    if (wdt == MOE_F32) return set_error(MOE_ERR_UNSUPPORTED, "bf16 activations need bf16 or fp8 weights");
+    if (wdt != MOE_BF16 && wdt != MOE_FP8_E4M3) return set_error(MOE_ERR_INVALID_ARG, "unknown weight dtype %d", wdt);
+    moe_status st = check_fused(T, H, I, k, E, n_shared, act, wdt, split);
+    if (st != MOE_OK) return st;
+    if (wdt == MOE_FP8_E4M3 && (!w13_scale || !w2_scale))
+        return set_error(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !permuted_pair || !w13 || !w2 || !fc2_out)
+        return set_error(MOE_ERR_INVALID_ARG, "x, expert_offsets, permuted_pair, w13, w2 and fc2_out must be non-null");
+    return launch_ffn_fused(x, nullptr, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2,
+                            wdt, wdt == MOE_FP8_E4M3 ? w13_scale : nullptr,
+                            wdt == MOE_FP8_E4M3 ? w2_scale : nullptr, split, fc2_out,
+                            static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_fp8_fused(const uint8_t* xq, const float* x_scale, int T, int H, int I,
+                                    int k, int E, int n_shared, const int32_t* expert_offsets,
+                                    const int32_t* permuted_pair, const uint8_t* w13,
+                                    const uint8_t* w2, const float* w13_scale,
+                                    const float* w2_scale, int split, void* fc2_out, void* stream)
+{
+    moe_status st = check_fused(T, H, I, k, E, n_shared, MOE_FP8_E4M3, MOE_FP8_E4M3, split);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!xq || !x_scale || !expert_offsets || !permuted_pair || !w13 || !w2 || !w13_scale || !w2_scale ||
+        !fc2_out)
+        return set_error(MOE_ERR_INVALID_ARG,
+                         "xq, x_scale, expert_offsets, permuted_pair, w13, w2, their scales and fc2_out "
+                         "must be non-null");
+    return launch_ffn_fused(xq, x_scale, MOE_FP8_E4M3, T, H, I, k, E, n_shared, expert_offsets, permuted_pair,
+                            w13, w2, MOE_FP8_E4M3, w13_scale, w2_scale, split, fc2_out,
+                            static_cast<hipStream_t>(stream));
+}
+
 moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
                         const float* scales, int T, int k, int H, int n_shared, void* y,
                         int ydt, void* stream)

@@ -127,6 +127,10 @@ moe_status launch_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, int H,
                           int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
                           const uint8_t* w13, const uint8_t* w2, const float* w13_scale,
                           const float* w2_scale, void* fc2_out, void* ws, hipStream_t s);
+moe_status launch_ffn_fused(const void* x, const float* x_scale, int act, int T, int H, int I, int k,
+                            int E, int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
+                            const void* w13, const void* w2, int wdt, const float* w13_scale,
+                            const float* w2_scale, int split, void* fc2_out, hipStream_t s);
 moe_status launch_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* q, float* scale,
                                hipStream_t s);
 moe_status launch_finalize(const void* fc2_out, int dt, const int32_t* unpermute,

@@ -130,6 +130,33 @@ def test_expert_ffn_fp8_validation(L):
     assert f(600000, 7168, 2048, k=8, E=256) == UNSUPPORTED  # hq: 4.8M rows x 2048 > 4 GiB
 
 
+def test_expert_ffn_fused_validation(L):
+    p = C.c_void_p(16)
+    f = lambda T, H, I, act=1, wdt=1, s13=p, split=0, k=2, E=8: L.moe_expert_ffn_fused(  # noqa: E731
+        p, act, T, H, I, k, E, 0, p, p, p, p, wdt, s13, p, split, p, None)
+    assert f(16, 100, 128) == UNSUPPORTED                 # H % 128
+    assert f(16, 128, 96) == UNSUPPORTED                  # I % 128
+    assert f(16, 128, 2176) == UNSUPPORTED                # I above the LDS-resident h limit
+    assert "limit 2048" in err(L)
+    assert f(16, 128, 128, act=0, wdt=0) == UNSUPPORTED   # fp32 layers: two-call path only
+    assert f(16, 128, 128, act=2) == INVALID              # fp8 x goes through the fp8 entry
+    assert f(16, 128, 128, wdt=0) == UNSUPPORTED          # bf16 x with fp32 weights
+    assert f(16, 128, 128, wdt=2, s13=None) == INVALID    # fp8 weights need scales
+    assert f(16, 128, 128, split=-1) == INVALID
+    assert f(16, 128, 128, split=65) == INVALID
+    assert f(16, 128, 128, k=9) == INVALID
+    assert f(0, 128, 128) == OK                           # T = 0: nothing launched
+    assert f(300000, 7168, 2048, k=8, E=256) == UNSUPPORTED  # x above 4 GiB
+    g = lambda T, H, I, s13=p, split=0: L.moe_expert_ffn_fp8_fused(  # noqa: E731
+        p, p, T, H, I, 2, 8, 0, p, p, p, p, s13, p, split, p, None)
+    assert g(16, 100, 128) == UNSUPPORTED
+    assert g(16, 128, 4096) == UNSUPPORTED                # I limit
+    assert g(16, 128, 128, s13=None) == INVALID
+    assert g(16, 128, 128, split=-2) == INVALID
+    assert g(-1, 128, 128) == INVALID
+    assert g(0, 128, 128) == OK
+
+
 def test_finalize_validation(L):
     p = C.c_void_p(16)
     assert L.moe_finalize(p, 1, p, p, 4, 2, 100, 0, p, 1, None) == UNSUPPORTED  # H % 8

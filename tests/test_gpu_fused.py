@@ -1,0 +1,234 @@
+"""GPU parity of the fused FC1+FC2 entry points (moe_expert_ffn_fused,
+moe_expert_ffn_fp8_fused: one kernel, h kept in LDS) through the C ABI.
+
+The fused kernel performs, per output element, the same operations in the
+same order as the two-call path (same MFMA forms and K order, same rounding of
+h to bf16 or to e4m3 codes with the same per-128 scales), so the bar against
+moe_expert_ffn / moe_expert_ffn_fp8 is bit-identical output.  The two-call
+path is itself held to the oracle by test_gpu_parity.py / test_gpu_fp8act.py;
+here the fused output is also compared with the oracle directly (relative L2
+1e-2, as for the two-call bf16 and fp8 paths).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mixture_experts_layer_07_amd as moe
+from mixture_experts_layer_07_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = 1e-2
+PRECISIONS = ["bf16", "w8", "a8"]  # bf16 x bf16, bf16 x fp8 weights, fp8 x fp8
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def host(t):
+    return t.detach().cpu()
+
+
+def workload(prec, T, H, I, E, k, n_shared=0, method=4, **kw):
+    return wl.Workload(f"fused_{prec}_{T}", 98, T=T, H=H, E=E, I=I, k=k, method=method, act="bf16",
+                       wdt="bf16" if prec == "bf16" else "fp8", n_shared=n_shared, **kw)
+
+
+def routed(w, inp):
+    ids, sc, _ = oracle.route(inp["logits"], w.k, w.method, w.n_group, w.topk_group, inp["bias"],
+                              w.scaling, bool(w.flags & wl.ROUTE_FLAG_RENORMALIZE))
+    off, pp, _ = oracle.permute(ids, w.E, w.n_shared)
+    return off, pp
+
+
+def both_paths(w, prec, g, off, pp, splits=(0,)):
+    """fc2_out of the two-call path and of the fused kernel for each split."""
+    off_d, pp_d = torch.as_tensor(off).to(DEV), torch.as_tensor(pp).to(DEV)
+    if prec == "a8":
+        xq, xs = moe.quantize_fp8(g["x"])
+        ref = moe.expert_ffn_fp8(xq, xs, off_d, pp_d, g["w13"], g["w2"], g["w13_scale"], g["w2_scale"],
+                                 w.k, w.E, w.n_shared)
+        fused = [moe.expert_ffn_fp8_fused(xq, xs, off_d, pp_d, g["w13"], g["w2"], g["w13_scale"],
+                                          g["w2_scale"], w.k, w.E, w.n_shared, split=s) for s in splits]
+    else:
+        ref = moe.expert_ffn(g["x"], off_d, pp_d, g["w13"], g["w2"], w.k, w.E, w.n_shared,
+                             g["w13_scale"], g["w2_scale"])
+        fused = [moe.expert_ffn_fused(g["x"], off_d, pp_d, g["w13"], g["w2"], w.k, w.E, w.n_shared,
+                                      g["w13_scale"], g["w2_scale"], split=s) for s in splits]
+    torch.cuda.synchronize()
+    return ref, fused
+
+
+def assert_same(a, b, what):
+    if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+        d = (a.float() - b.float()).abs()
+        n = int((a.view(torch.int16) != b.view(torch.int16)).sum())
+        raise AssertionError(f"{what}: {n} elements differ, max |diff| {float(d.max()):.3e}")
+
+
+def oracle_rows(w, prec, inp, off, pp, rows):
+    W = oracle.Weights(inp["w13"], inp["w2"], w.wdt, inp["w13_scale"], inp["w2_scale"])
+    if prec == "a8":
+        qo, so = oracle.quantize_fp8(inp["x"].view(torch.int16).numpy(), "bf16")
+        return oracle.expert_rows(W, qo, "fp8", w.T, w.k, w.E, w.n_shared, off, pp, rows, x_scale=so)
+    return oracle.expert_rows(W, inp["x"], "bf16", w.T, w.k, w.E, w.n_shared, off, pp, rows)
+
+
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_fused_small_bit_identical_and_oracle(prec):
+    # ~19 rows per group (two 16-row tiles with a ragged tail), a 300-row
+    # shared group, several FC1 and FC2 sub-tiles, splits 0 (automatic) to 3
+    w = workload(prec, 300, 384, 256, 32, 2, n_shared=1)
+    inp = wl.make_inputs(w, 1)
+    off, pp = routed(w, inp)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    ref, fused = both_paths(w, prec, g, off, pp, splits=(0, 1, 2, 3))
+    for s, f in zip((0, 1, 2, 3), fused):
+        assert_same(f, ref, f"{prec} split {s}")
+    rows = np.arange(w.R, dtype=np.int32)
+    err = rel_l2(host(fused[0]).double().numpy(), oracle_rows(w, prec, inp, off, pp, rows))
+    print(f"[fused {prec}] rel L2 vs oracle {err:.3e}", flush=True)
+    assert err < TOL
+
+
+ROW_TILE_EDGES = [0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 100, 255, 256, 257]
+
+
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_fused_row_tile_boundaries(prec):
+    """Groups of 0, 1, 15/16/17, ... rows (16-row tiles), one-hot routing."""
+    counts = ROW_TILE_EDGES
+    E, T = len(counts), sum(counts)
+    w = workload(prec, T, 256, 384, E, 1, method=0)
+    inp = wl.make_inputs(w, 2)
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(2).shuffle(owner)
+    logits = torch.full((T, E), -5.0)
+    logits[torch.arange(T), torch.from_numpy(owner)] = 5.0
+    inp["logits"] = logits
+    off, pp = routed(w, inp)
+    assert np.array_equal(np.diff(off), counts)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    ref, fused = both_paths(w, prec, g, off, pp, splits=(0, 2))
+    for f in fused:
+        assert_same(f, ref, prec)
+    rows = np.arange(0, w.R, 5, dtype=np.int32)
+    assert rel_l2(host(fused[0]).double().numpy()[rows], oracle_rows(w, prec, inp, off, pp, rows)) < TOL
+
+
+@pytest.mark.parametrize("prec", PRECISIONS)
+@pytest.mark.parametrize("H,I", [(128, 128), (640, 1920), (384, 2048), (2048, 640)])
+def test_fused_shape_edges(prec, H, I):
+    """I = 128 (one FC2 K step) and I = 2048 (the LDS limit); H = 640 leaves a
+    partial 256-column FC2 sub-tile; split above the number of FC2 sub-tiles is
+    clamped."""
+    w = workload(prec, 70, H, I, 6, 2, n_shared=1)
+    inp = wl.make_inputs(w, 3)
+    off, pp = routed(w, inp)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    ref, fused = both_paths(w, prec, g, off, pp, splits=(0, 1, 64))
+    for s, f in zip((0, 1, 64), fused):
+        assert_same(f, ref, f"{prec} H={H} I={I} split {s}")
+
+
+@pytest.mark.parametrize("prec", PRECISIONS)
+def test_fused_degenerate(prec):
+    """One token, one expert; k = E with two shared experts."""
+    for (T, H, I, E, k, ns) in [(1, 128, 128, 1, 1, 0), (3, 256, 128, 4, 4, 2)]:
+        w = workload(prec, T, H, I, E, k, n_shared=ns)
+        inp = wl.make_inputs(w, 5)
+        off, pp = routed(w, inp)
+        g = {kk: (None if v is None else v.to(DEV)) for kk, v in inp.items()}
+        ref, fused = both_paths(w, prec, g, off, pp, splits=(0, 1))
+        for f in fused:
+            assert_same(f, ref, f"{prec} T={T} E={E}")
+        rows = np.arange(w.R, dtype=np.int32)
+        assert rel_l2(host(fused[0]).double().numpy(), oracle_rows(w, prec, inp, off, pp, rows)) < TOL
+
+
+FULL = [("dsv3_decode", "bf16"), ("dsv3_decode", "a8"), ("dsv3_prefill", "bf16"),
+        ("dsv3_prefill", "a8"), ("qwen3_fp8", "w8"), ("qwen3_fp8", "a8")]
+
+
+@pytest.mark.parametrize("name,prec", FULL)
+def test_fused_full_workloads_bit_identical(name, prec):
+    """The full-size DeepSeek-V3 decode / prefill and Qwen3-shaped layers, with
+    the split bench.py times (automatic) and split 1: the fused kernel's
+    fc2_out equals the two-call path's bit for bit; sampled rows against the
+    oracle."""
+    w = wl.WORKLOADS[name]
+    if prec == "a8" and w.wdt != "fp8":
+        w = w.with_(wdt="fp8")
+    print(f"[fused full] {name} {prec} T={w.T} H={w.H} E={w.E} I={w.I}", flush=True)
+    x = wl.make_x(w)
+    logits = wl.make_logits(w, x)
+    bias = wl.make_bias(w)
+    w13, w2, s13, s2 = wl.make_weights(w, 0, DEV)
+    inp = dict(x=x, logits=logits, bias=bias)
+    off, pp = routed(w, inp)
+    g = dict(x=x.to(DEV), w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
+    ref, fused = both_paths(w, prec, g, off, pp, splits=(0, 1))
+    for s, f in zip((0, 1), fused):
+        assert_same(f, ref, f"{name} {prec} split {s}")
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, w.R - 1], rng.choice(w.R, 24, replace=False)])).astype(np.int32)
+    inp_o = dict(x=x, w13=host(w13), w2=host(w2), w13_scale=None if s13 is None else host(s13),
+                 w2_scale=None if s2 is None else host(s2))
+    err = rel_l2(host(fused[0]).double().numpy()[rows], oracle_rows(w, prec, inp_o, off, pp, rows))
+    print(f"[fused full] {name} {prec}: rel L2 vs oracle {err:.3e} over {len(rows)} rows", flush=True)
+    assert err < TOL
+
+
+@pytest.mark.parametrize("prec", ["bf16", "a8"])
+def test_fused_layer_and_graph_capture(prec):
+    """MoELayer(fused=True) equals the two-call layer bit for bit, and its
+    captured HIP graph replays to the eager result."""
+    w = workload(prec, 500, 256, 256, 16, 4, n_shared=1, method=2, n_group=4, topk_group=2,
+                 scaling=2.5, bias=True)
+    fp8 = prec == "a8"
+    inputs = [{k: (None if v is None else v.to(DEV)) for k, v in wl.make_inputs(w, s).items()}
+              for s in (21, 22)]
+    two = moe.layer_for_workload(w, DEV, fp8_act=fp8)
+    one = moe.layer_for_workload(w, DEV, fp8_act=fp8, fused=True)
+    run = lambda L, i: L(i["x"], i["logits"], i["w13"], i["w2"], i["bias"], i["w13_scale"],  # noqa: E731
+                         i["w2_scale"])
+    y2 = run(two, inputs[0]).clone()
+    y1 = run(one, inputs[0]).clone()
+    torch.cuda.synchronize()
+    assert_same(y1, y2, "layer")
+    g = {k: (None if v is None else v.clone()) for k, v in inputs[0].items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(one, g)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y_graph = run(one, g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = inputs[rep % 2]
+        for k, v in src.items():
+            if v is not None:
+                g[k].copy_(v)
+        torch.cuda.synchronize()
+        eager = run(two, src).clone()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_same(y_graph, eager, f"replay {rep}")
+
+
+def test_fused_rejects_large_intermediate():
+    w = workload("bf16", 8, 128, 2176, 2, 1)
+    inp = {k: (None if v is None else v.to(DEV)) for k, v in wl.make_inputs(w, 6).items()}
+    off = torch.zeros(w.E + 1, dtype=torch.int32, device=DEV)
+    pp = torch.zeros(w.P, dtype=torch.int32, device=DEV)
+    with pytest.raises(moe.MoeError) as e:
+        moe.expert_ffn_fused(inp["x"], off, pp, inp["w13"], inp["w2"], w.k, w.E)
+    assert e.value.status == 2  # MOE_ERR_UNSUPPORTED
