@@ -257,10 +257,10 @@ moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, in
  *             larger I is MOE_ERR_UNSUPPORTED.
  *  split      workgroups that share one 16-row tile: each computes the tile's
  *             h (FC1 repeated) and takes every split-th 128- or 256-column
- *             block of its FC2.  0 picks it from the shape (about two work
- *             items per CU); values above the number of FC2 column blocks are
- *             clamped to it; negative values and values above 64 are
- *             MOE_ERR_INVALID_ARG.  Results do not depend on it.
+ *             block of its FC2.  0 = automatic (currently 1: each extra split
+ *             re-reads the expert's whole w13).  Values above the number of
+ *             FC2 column blocks are clamped to it; negative values and values
+ *             above 64 are MOE_ERR_INVALID_ARG.  Results do not depend on it.
  *  other arguments as for moe_expert_ffn; there is no workspace.
  * Limits: x and one expert's w13 below 4 GiB.
  */

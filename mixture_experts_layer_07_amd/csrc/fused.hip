@@ -585,15 +585,10 @@ moe_status run_fused(FusedArgs a, int R, hipStream_t s)
         occ = n;
     }
     const int n2 = (a.H + C::BN - 1) / C::BN;
-    if (a.nsplit <= 0) {
-        // Enough items for two per CU: the row tiles (about R / BM plus one
-        // partial tile per group) times the split, at most one FC2 sub-tile
-        // per workgroup.
-        const long tiles = (long)R / C::BM + a.G / 2 + 1;
-        const long want = 2L * device_cu_count();
-        long ns = (want + tiles - 1) / tiles;
-        a.nsplit = (int)(ns < 1 ? 1 : ns > n2 ? n2 : ns);
-    }
+    // Automatic: one workgroup per row tile.  Every further split re-reads the
+    // expert's whole w13 to recompute h; measured on the DeepSeek-V3 and
+    // Qwen3-shaped layers, time grows about linearly with the split.
+    if (a.nsplit <= 0) a.nsplit = 1;
     if (a.nsplit > n2) a.nsplit = n2;
     const long max_items = ((long)R / C::BM + a.G) * a.nsplit;
     long grid = (long)device_cu_count() * occ;
@@ -607,14 +602,23 @@ moe_status run_fused(FusedArgs a, int R, hipStream_t s)
     return launch_status("fused_ffn_kernel");
 }
 
-// Shapes: 16-row tiles (h of 16 rows x 2048 channels is 64 KB in bf16, so
-// with the ring it fills the LDS), 4 waves splitting the columns.  bf16:
-// 128-column sub-tiles and a 4-deep ring; fp8 weights: 6-deep (half the bytes
-// per stage); fp8 activations: 256-column sub-tiles (one 128-channel block of
-// h each) and a 3-deep ring.
+// Shapes, measured on MI355X.  16-row tiles: h of 16 rows x 2048 channels is
+// 64 KB in bf16, which with the ring fills the LDS; 4 waves split the columns.
+//   bf16:         128-column sub-tiles, 4-deep ring (256 columns with a 2-deep
+//                 ring: DeepSeek-V3 decode +29%; a 5-deep ring: no gain);
+//   fp8 weights:  256-column sub-tiles, 3-deep ring (128 columns, 6-deep:
+//                 DeepSeek-V3 decode 5.4 -> 3.4 ms, Qwen3-shaped 5.8 -> 3.4 ms);
+//   fp8 x fp8:    256-column sub-tiles (one 128-channel block of h each).  h
+//                 codes take half the bytes, so groups averaging 64 rows or
+//                 more get 32-row tiles (each expert's weights stream through
+//                 the CUs half as often; 2-deep ring: DeepSeek-V3 prefill 17.8
+//                 -> 13.7 ms), smaller ones 16-row tiles with a 3-deep ring
+//                 (32-row tiles: DeepSeek-V3 decode 2.6 -> 3.5 ms).
 using FusedBf16 = FusedCfg<16, 128, 4, 4, false, false, 2 * MOE_FUSED_MAX_I>;
-using FusedW8 = FusedCfg<16, 128, 4, 6, true, false, 2 * MOE_FUSED_MAX_I>;
+using FusedW8 = FusedCfg<16, 256, 4, 3, true, false, 2 * MOE_FUSED_MAX_I>;
 using FusedA8 = FusedCfg<16, 256, 4, 3, true, true, MOE_FUSED_MAX_I>;
+using FusedA8Tall = FusedCfg<32, 256, 4, 2, true, true, MOE_FUSED_MAX_I>;
+constexpr int kTallRows = 64;  // average rows per group from which fp8 x fp8 takes 32-row tiles
 
 }  // namespace
 
@@ -636,7 +640,8 @@ moe_status launch_ffn_fused(const void* x, const float* x_scale, int act, int T,
     a.T = T; a.k = k; a.E = E; a.G = E + n_shared; a.H = H; a.I = I;
     a.nsplit = split;
     const int R = T * k + n_shared * T;
-    if (act == MOE_FP8_E4M3) return run_fused<FusedA8>(a, R, s);
+    if (act == MOE_FP8_E4M3)
+        return R >= kTallRows * a.G ? run_fused<FusedA8Tall>(a, R, s) : run_fused<FusedA8>(a, R, s);
     if (wdt == MOE_FP8_E4M3) return run_fused<FusedW8>(a, R, s);
     return run_fused<FusedBf16>(a, R, s);
 }
