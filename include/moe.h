@@ -246,7 +246,7 @@ moe_status moe_expert_ffn_fp8(const uint8_t* xq, const float* x_scale, int T, in
 /*
  * moe_expert_ffn_fused -- moe_expert_ffn as ONE kernel that keeps h on chip:
  * FC1 and FC2 fused, the intermediate never written to memory (the FC12 form
- * of the TensorRT-LLM page, section "MoE 后端:同一个接口,多种实现").  A
+ * of the TensorRT-LLM page, section "后端的三种形态与两个调度器家族").  A
  * workgroup takes 16 rows of one group, computes their h [16, I] into LDS
  * (FC1 + SwiGLU over all I channels), then their FC2 rows from it.
  * Results are bit-identical to moe_expert_ffn for the same arguments.

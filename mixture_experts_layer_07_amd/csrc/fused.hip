@@ -2,7 +2,7 @@
 // group as ONE kernel in which the intermediate h never leaves the CU.
 //
 // The fused FC1+FC2 form is the one the TensorRT-LLM page lists as its
-// CuteDslFc12 backend (section "MoE 后端:同一个接口,多种实现": FC1 and FC2 in
+// CuteDslFc12 backend (section "后端的三种形态与两个调度器家族": FC1 and FC2 in
 // one kernel, the intermediate kept on chip).  Here a work item is one tile
 // of BM rows of one group; its workgroup
 //   phase 1: computes h[BM, I] = silu(x W1^T) * (x W3^T) in 2I/BN column
