@@ -102,12 +102,18 @@ __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b)
                                                             127, 0, 127);
 }
 
-// 32 fp8 codes of one row at K bytes [32 g, 32 g + 32) of a staged 128-byte
-// row: logical chunks 2g and 2g+1.
+// Lane group g's 32 fp8 codes of one row of a staged 128-byte K block: logical
+// chunks g and g+4 (K bytes [16g, 16g+16) and [64+16g, 64+16g+16)).  The MFMA
+// sums over the whole block, so any assignment of K positions to lane groups
+// is valid when both operands use the same one; with this one every
+// ds_read_b128 has the lane groups on four consecutive chunks, the pattern of
+// the bf16 fragment reads, which is free of bank conflicts on gfx950.
+// (Chunks 2g and 2g+1 measured 1.1e9 conflict cycles in the fp8 x fp8
+// DeepSeek-V3 prefill FC1.)
 __device__ __forceinline__ i32x8_t lds_row32(const char* base, int row, int g)
 {
-    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, 2 * g));
-    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, 2 * g + 1));
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, g));
+    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + dma_off(row, g + 4));
     return i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 

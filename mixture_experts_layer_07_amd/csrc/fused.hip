@@ -363,9 +363,10 @@ __global__ __launch_bounds__(C::NT) void fused_ffn_kernel(FusedArgs a)
                             fa[mi] = lds_row32(la, row, g4);
                         } else {
                             sa = hsc[row * C::HSN + kt];
+                            // the K positions of lds_row32: chunks g4 and g4+4
                             const char* hr = hbuf + row * C::HPITCH + kt * 128;
-                            const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(hr + (((2 * g4) ^ (row & 7)) << 4));
-                            const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(hr + (((2 * g4 + 1) ^ (row & 7)) << 4));
+                            const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(hr + ((g4 ^ (row & 7)) << 4));
+                            const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(hr + (((g4 + 4) ^ (row & 7)) << 4));
                             fa[mi] = i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                              (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
                         }
