@@ -81,17 +81,16 @@ struct FusedCfg {
     static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
     static constexpr int WTN = BN / WN;
     static constexpr int MI = BM / 16, NI = WTN / 16;
-    static constexpr int HE = A8 ? 1 : 2;                  // bytes per h element
     static constexpr int HROW = HROW_;
     static constexpr int HPITCH = HROW + 128;              // odd multiple of 128 B: the ring's bank pattern
     static constexpr int HSN = A8 ? HROW / 128 : 1;        // h scales per row
     static constexpr int LDS_BYTES = S * STAGE + BM * HPITCH + BM * HSN * 4 + BM * WN * 4 +
                                      2 * (kMaxGroups + 1) * 4;
-    static_assert(BM % 16 == 0 && BM <= 64 && BM % 8 == 0, "row tile");
+    static_assert(BM % 16 == 0 && BM <= 64, "row tile");
     static_assert(WTN % 32 == 0, "a wave holds whole gate/up column pairs");
     static_assert(!A8 || BN == 256, "A8: one FC1 sub-tile = one 128-channel block of h");
     static_assert(B_OPS % NW == 0, "phase-2 transfers split evenly");
-    static_assert(HROW % 128 == 0, "h row");
+    static_assert(HROW % 128 == 0 && (HPITCH / 128) % 2 == 1, "h row: an odd number of 128-byte units");
     static_assert(S >= 2 && S <= 8 && LDS_BYTES <= 160 * 1024, "LDS");
 };
 
