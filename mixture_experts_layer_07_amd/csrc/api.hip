@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -33,23 +34,23 @@ moe_status launch_status(const char* what)
 
 int device_cu_count()
 {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // ------------------------------------------------------------------ timing
 namespace {
 struct TimingState {
     std::mutex mu;
-    bool enabled = false;
+    std::atomic<bool> enabled{false};
     struct Rec { int kid; hipEvent_t a, b; };
     std::vector<Rec> pending;
     std::vector<hipEvent_t> free_events;
@@ -74,24 +75,29 @@ hipEvent_t take_event(TimingState& t)
 }
 }  // namespace
 
-TimedLaunch::TimedLaunch(int kid, hipStream_t s) : kid_(kid), s_(s), slot_(-1)
+TimedLaunch::TimedLaunch(int kid, hipStream_t s) : kid_(kid), s_(s)
 {
     TimingState& t = timing();
-    if (!t.enabled) return;
+    if (!t.enabled.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> g(t.mu);
     hipEvent_t a = take_event(t), b = take_event(t);
-    if (!a || !b) return;
-    t.pending.push_back({kid, a, b});
-    slot_ = (int)t.pending.size() - 1;
-    (void)hipEventRecord(a, s);
+    if (!a || !b) {
+        if (a) t.free_events.push_back(a);
+        if (b) t.free_events.push_back(b);
+        return;
+    }
+    a_ = a;
+    b_ = b;
+    (void)hipEventRecord(a_, s_);
 }
 
 TimedLaunch::~TimedLaunch()
 {
-    if (slot_ < 0) return;
+    if (!b_) return;
     TimingState& t = timing();
+    (void)hipEventRecord(b_, s_);
     std::lock_guard<std::mutex> g(t.mu);
-    (void)hipEventRecord(t.pending[slot_].b, s_);
+    t.pending.push_back({kid_, a_, b_});
 }
 
 }  // namespace moe
@@ -368,8 +374,7 @@ moe_status moe_finalize(const void* fc2_out, int dt, const int32_t* unpermute,
 moe_status moe_timing_enable(int enable)
 {
     TimingState& t = timing();
-    std::lock_guard<std::mutex> g(t.mu);
-    t.enabled = enable != 0;
+    t.enabled.store(enable != 0, std::memory_order_relaxed);
     return MOE_OK;
 }
 

@@ -97,12 +97,14 @@ __device__ __forceinline__ uint32_t fp8x4_code(const float (&v)[4], float s)
 }
 
 // ------------------------------------------------------------ host side
+// Brackets one launch with a pair of events while timing is enabled; the
+// pair joins the pending list only once both are recorded.
 struct TimedLaunch {
     TimedLaunch(int kid, hipStream_t s);
     ~TimedLaunch();
     int kid_;
     hipStream_t s_;
-    int slot_;
+    hipEvent_t a_ = nullptr, b_ = nullptr;
 };
 
 int device_cu_count();                        // CUs of the current device

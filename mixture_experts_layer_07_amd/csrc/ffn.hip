@@ -905,12 +905,12 @@ moe_status run_dma_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream
                         int take_max = 0)
 {
     auto kern = dma_gemm_kernel<MODE, C>;
-    static int occ = -1;
-    if (occ < 0) {
+    static const int occ = [] {  // once per kernel (thread-safe static initialisation)
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, 0) != hipSuccess || n < 1) n = 1;
-        occ = n;
-    }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dma_gemm_kernel<MODE, C>, C::NT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
     args.lo_rows = lo_rows;
     args.hi_rows = hi_rows;
     args.give_max = give_max;
@@ -934,12 +934,12 @@ template <class AT, class WT, int MODE, class C>
 moe_status run_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s, int kid)
 {
     auto kern = grouped_gemm_kernel<AT, WT, MODE, C>;
-    static int occ = -1;
-    if (occ < 0) {
+    static const int occ = [] {  // once per kernel (thread-safe static initialisation)
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, 0) != hipSuccess || n < 1) n = 1;
-        occ = n;
-    }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_kernel<AT, WT, MODE, C>, C::NT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
     args.lo_rows = lo_rows;
     args.hi_rows = hi_rows;
     const long max_tiles = (long)(R / C::BM + args.G) * ((args.N + C::BN - 1) / C::BN);

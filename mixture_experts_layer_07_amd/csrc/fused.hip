@@ -578,12 +578,12 @@ template <class C>
 moe_status run_fused(FusedArgs a, int R, hipStream_t s)
 {
     auto kern = fused_ffn_kernel<C>;
-    static int occ = -1;
-    if (occ < 0) {
+    static const int occ = [] {  // once per kernel (thread-safe static initialisation)
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, C::NT, 0) != hipSuccess || n < 1) n = 1;
-        occ = n;
-    }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_ffn_kernel<C>, C::NT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
     const int n2 = (a.H + C::BN - 1) / C::BN;
     // Automatic: one workgroup per row tile.  Every further split re-reads the
     // expert's whole w13 to recompute h; measured on the DeepSeek-V3 and
