@@ -155,7 +155,10 @@ moe_status moe_permute(const int32_t* ids, int T, int k, int E, int n_shared,
  *
  *  x          device [T, H] in `act` (MOE_F32 or MOE_BF16).
  *  H, I       hidden and intermediate sizes, multiples of 128.
- *  expert_offsets, permuted_pair   as produced by moe_permute.
+ *  expert_offsets, permuted_pair   as produced by moe_permute for the same
+ *             T, k, E, n_shared.  Their contents are device data and are not
+ *             checked: other values may make the kernels read or write out of
+ *             bounds.  The same holds for every FFN entry point below.
  *  w13        device [E + n_shared, 2I, H] in `wdt`: rows [0, I) are the gate
  *             projection W1, rows [I, 2I) the up projection W3.
  *  w2         device [E + n_shared, H, I] in `wdt`.
@@ -185,7 +188,9 @@ moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, in
  * FC2 (TensorRT-LLM page, sections "通信与计算融合的方向" and "小结").
  *
  *  fc2_out    device [T*k + n_shared*T, H] in `dt` (MOE_F32 or MOE_BF16).
- *  unpermute, scales   from moe_permute / moe_route.
+ *  unpermute, scales   from moe_permute / moe_route for the same T, k, E,
+ *             n_shared (unpermute is not checked: other values may make the
+ *             gather read out of bounds).
  *  y          device [T, H] out in `ydt` (MOE_F32 or MOE_BF16).
  *  H          multiple of 8.
  */

@@ -89,6 +89,23 @@ def _stream(device) -> C.c_void_p:
     return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _call(fn: str, device, *args):
+    """Calls library entry `fn` with `device` current and its current stream
+    appended; tensor arguments become device pointers and must all live on
+    `device` (the kernels run on the current device)."""
+    device = torch.device(device)
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            if a.device != device:
+                raise ValueError(f"{fn}: a tensor on {a.device}, expected {device}")
+            a = _ptr(a)
+        conv.append(a)
+    with torch.cuda.device(device):
+        st = getattr(lib(), fn)(*conv, _stream(device))
+    _check(fn, st)
+
+
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -131,9 +148,8 @@ def route(logits, k, method, n_group=1, topk_group=1, bias=None, scaling=1.0,
         _dev(ids, "ids", torch.int32, (T, k))
         _dev(scales, "scales", torch.float32, (T, k))
     flags = ROUTE_FLAG_RENORMALIZE if renormalize else 0
-    _check("moe_route", lib().moe_route(_ptr(logits), T, E, method, k, n_group, topk_group,
-                                        _ptr(bias), float(scaling), flags, _ptr(ids),
-                                        _ptr(scales), _stream(logits.device)))
+    _call("moe_route", logits.device, logits, T, E, method, k, n_group, topk_group, bias,
+          float(scaling), flags, ids, scales)
     return ids, scales
 
 
@@ -153,8 +169,8 @@ def permute(ids, E, n_shared=0, ws=None, out=None):
         _dev(up, "unpermute", torch.int32, (T * k,))
     if ws is None:
         ws = alloc_workspace(T, k, E, n_shared, 128, 128, torch.bfloat16, d)
-    _check("moe_permute", lib().moe_permute(_ptr(ids), T, k, E, n_shared, _ptr(off), _ptr(pp),
-                                            _ptr(up), _ptr(ws), ws.numel(), _stream(d)))
+    _dev(ws, "ws", torch.uint8)
+    _call("moe_permute", d, ids, T, k, E, n_shared, off, pp, up, ws, ws.numel())
     return off, pp, up
 
 
@@ -180,10 +196,9 @@ def expert_ffn(x, expert_offsets, permuted_pair, w13, w2, k, E, n_shared=0, w13_
         _dev(out, "fc2_out", x.dtype, (R, H))
     if ws is None:
         ws = alloc_workspace(T, k, E, n_shared, H, I, x.dtype, x.device)
-    _check("moe_expert_ffn", lib().moe_expert_ffn(
-        _ptr(x), _DT[x.dtype], T, H, I, k, E, n_shared, _ptr(expert_offsets),
-        _ptr(permuted_pair), _ptr(w13), _ptr(w2), _DT[w13.dtype], _ptr(w13_scale),
-        _ptr(w2_scale), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)))
+    _dev(ws, "ws", torch.uint8)
+    _call("moe_expert_ffn", x.device, x, _DT[x.dtype], T, H, I, k, E, n_shared, expert_offsets,
+          permuted_pair, w13, w2, _DT[w13.dtype], w13_scale, w2_scale, out, ws, ws.numel())
     return out
 
 
@@ -198,8 +213,7 @@ def quantize_fp8(x, out=None):
         xq, xs = out
         _dev(xq, "xq", torch.float8_e4m3fn, (rows, cols))
         _dev(xs, "x_scale", torch.float32, (rows, cols // 128))
-    _check("moe_quantize_fp8", lib().moe_quantize_fp8(_ptr(x), _DT[x.dtype], rows, cols, _ptr(xq),
-                                                      _ptr(xs), _stream(x.device)))
+    _call("moe_quantize_fp8", x.device, x, _DT[x.dtype], rows, cols, xq, xs)
     return xq, xs
 
 
@@ -225,10 +239,9 @@ def expert_ffn_fp8(xq, x_scale, expert_offsets, permuted_pair, w13, w2, w13_scal
         _dev(out, "fc2_out", torch.bfloat16, (R, H))
     if ws is None:
         ws = alloc_workspace(T, k, E, n_shared, H, I, torch.float8_e4m3fn, xq.device)
-    _check("moe_expert_ffn_fp8", lib().moe_expert_ffn_fp8(
-        _ptr(xq), _ptr(x_scale), T, H, I, k, E, n_shared, _ptr(expert_offsets),
-        _ptr(permuted_pair), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale), _ptr(out),
-        _ptr(ws), ws.numel(), _stream(xq.device)))
+    _dev(ws, "ws", torch.uint8)
+    _call("moe_expert_ffn_fp8", xq.device, xq, x_scale, T, H, I, k, E, n_shared, expert_offsets,
+          permuted_pair, w13, w2, w13_scale, w2_scale, out, ws, ws.numel())
     return out
 
 
@@ -253,10 +266,8 @@ def expert_ffn_fused(x, expert_offsets, permuted_pair, w13, w2, k, E, n_shared=0
         out = torch.empty((R, H), dtype=torch.bfloat16, device=x.device)
     else:
         _dev(out, "fc2_out", torch.bfloat16, (R, H))
-    _check("moe_expert_ffn_fused", lib().moe_expert_ffn_fused(
-        _ptr(x), BF16, T, H, I, k, E, n_shared, _ptr(expert_offsets), _ptr(permuted_pair),
-        _ptr(w13), _ptr(w2), _DT[w13.dtype], _ptr(w13_scale), _ptr(w2_scale), int(split),
-        _ptr(out), _stream(x.device)))
+    _call("moe_expert_ffn_fused", x.device, x, BF16, T, H, I, k, E, n_shared, expert_offsets,
+          permuted_pair, w13, w2, _DT[w13.dtype], w13_scale, w2_scale, int(split), out)
     return out
 
 
@@ -281,10 +292,8 @@ def expert_ffn_fp8_fused(xq, x_scale, expert_offsets, permuted_pair, w13, w2, w1
         out = torch.empty((R, H), dtype=torch.bfloat16, device=xq.device)
     else:
         _dev(out, "fc2_out", torch.bfloat16, (R, H))
-    _check("moe_expert_ffn_fp8_fused", lib().moe_expert_ffn_fp8_fused(
-        _ptr(xq), _ptr(x_scale), T, H, I, k, E, n_shared, _ptr(expert_offsets),
-        _ptr(permuted_pair), _ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale), int(split),
-        _ptr(out), _stream(xq.device)))
+    _call("moe_expert_ffn_fp8_fused", xq.device, xq, x_scale, T, H, I, k, E, n_shared,
+          expert_offsets, permuted_pair, w13, w2, w13_scale, w2_scale, int(split), out)
     return out
 
 
@@ -302,9 +311,8 @@ def finalize(fc2_out, unpermute, scales, n_shared=0, out_dtype=None, out=None):
         out = torch.empty((T, H), dtype=ydt, device=fc2_out.device)
     else:
         _dev(out, "y", ydt, (T, H))
-    _check("moe_finalize", lib().moe_finalize(_ptr(fc2_out), _DT[fc2_out.dtype], _ptr(unpermute),
-                                              _ptr(scales), T, k, H, n_shared, _ptr(out),
-                                              _DT[ydt], _stream(fc2_out.device)))
+    _call("moe_finalize", fc2_out.device, fc2_out, _DT[fc2_out.dtype], unpermute, scales, T, k, H,
+          n_shared, out, _DT[ydt])
     return out
 
 

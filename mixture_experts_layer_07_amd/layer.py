@@ -48,6 +48,9 @@ class MoELayer:
             self.x_scale = torch.empty((T, H // 128), dtype=torch.float32, device=d)
 
     def forward(self, x, logits, w13, w2, bias=None, w13_scale=None, w2_scale=None):
+        """y [T, H] for x [T, H] and router logits [T, E] (fp32).  The result is
+        the layer's own output buffer: the next call overwrites it, so clone it
+        to keep it."""
         B.route(logits, self.k, self.method, self.n_group, self.topk_group, bias, self.scaling,
                 self.renormalize, out=(self.ids, self.scales))
         B.permute(self.ids, self.E, self.n_shared, ws=self.ws,

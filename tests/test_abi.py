@@ -192,3 +192,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def test_binding_rejects_tensors_on_another_device(L):
+    """Every entry runs on one device; the binding refuses a tensor elsewhere
+    before it makes the device current or calls the library."""
+    import torch
+    with pytest.raises(ValueError, match="moe_finalize: a tensor on cpu, expected cuda:0"):
+        binding._call("moe_finalize", "cuda:0", torch.zeros(8), 0, None, None, 1, 1, 8, 0, None, 0)
