@@ -140,6 +140,25 @@ def make_x(w: Workload, seed: int = 0) -> torch.Tensor:
     return torch.from_numpy(x).to(TORCH_DTYPE[w.act])
 
 
+def make_x_device(w: Workload, seed: int = 0, device="cuda", chunk_rows: int = 8192) -> torch.Tensor:
+    """Token activations [T, H] drawn N(0, 1) directly on `device` (seeded torch
+    generator, in row chunks) and rounded to the activation dtype: for shapes
+    whose host draw would be too large.  Other values than make_x's."""
+    x = torch.empty((w.T, w.H), dtype=TORCH_DTYPE[w.act], device=device)
+    gen = _torch_gen(seed, w.cid, _TID_X, 0, device)
+    for r0 in range(0, w.T, chunk_rows):
+        r1 = min(w.T, r0 + chunk_rows)
+        x[r0:r1] = torch.randn((r1 - r0, w.H), generator=gen, device=device, dtype=torch.float32)
+    return x
+
+
+def make_logits_direct(w: Workload, seed: int = 0) -> torch.Tensor:
+    """Router logits [T, E] drawn N(0, 1) directly (fp32, host), for shapes
+    where forming x . W_gate^T on the host would be too large."""
+    lg = _rng(seed, w.cid, _TID_WGATE).standard_normal((w.T, w.E), dtype=np.float32)
+    return torch.from_numpy(lg)
+
+
 def make_bias(w: Workload, seed: int = 0) -> Optional[torch.Tensor]:
     if not w.bias:
         return None

@@ -1,0 +1,181 @@
+"""GPU parity at the largest sizes the FFN entry points accept.
+
+The grouped-GEMM and fused kernels address x, h and one expert's weights with
+32-bit per-lane byte offsets added to a 64-bit base, and the host rejects any
+of these buffers at 4 GiB or above.  Each case puts one of them just below
+that limit (one more token, or 128 more channels, would be rejected) and
+compares against the oracle the tokens whose bytes lie highest: the last
+tokens of x and the tokens in the first and last rows of every group of h and
+fc2_out (the shared expert's rows come last).  Routing and permute are
+compared in full.  Inputs are seeded draws made on the device; the oracle
+gets the sampled tokens' rows only (it computes each token on its own).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mixture_experts_layer_07_amd as moe
+from mixture_experts_layer_07_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+LIM = 1 << 32
+
+
+def host(t):
+    return t.detach().cpu()
+
+
+def rel_l2_rows(got, ref):
+    """Largest per-row relative L2 error (each sampled token on its own)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)))
+
+
+def limit_workload(cid, T, H, I, E=2, k=1, n_shared=1, wdt="bf16"):
+    return wl.Workload(f"limit_{cid}", cid, T=T, H=H, E=E, I=I, k=k, method=wl.ROUTE_DEFAULT,
+                       wdt=wdt, n_shared=n_shared)
+
+
+def route_and_permute(w, layer, logits):
+    """Oracle routing and permute, checked bit-exact against the layer's."""
+    ids, sc, hard = oracle.route(logits, w.k, w.method)
+    assert hard == 0
+    assert np.array_equal(host(layer.ids).numpy(), ids)
+    assert np.max(np.abs(host(layer.scales).numpy() - sc) / np.abs(sc)) <= 1e-6
+    off, pp, up = oracle.permute(ids, w.E, w.n_shared)
+    assert np.array_equal(host(layer.offsets).numpy(), off)
+    assert np.array_equal(host(layer.permuted_pair).numpy(), pp)
+    assert np.array_equal(host(layer.unpermute).numpy(), up)
+    return ids, sc, off, pp
+
+
+def high_tokens(w, off, pp, n_random=6, seed=0):
+    """Tokens of the highest x rows and of each routed group's first and last
+    rows (the last shared rows belong to the last tokens), plus random ones."""
+    pick = {0, w.T - 1, w.T - 2}
+    for g in range(w.E):
+        if off[g + 1] > off[g]:
+            pick.add(int(pp[off[g]]) // w.k)
+            pick.add(int(pp[off[g + 1] - 1]) // w.k)
+    rng = np.random.default_rng(seed)
+    pick.update(rng.choice(w.T, size=n_random, replace=False).tolist())
+    return np.array(sorted(pick), np.int32)
+
+
+def rows_of(t, toks):
+    return host(t[torch.from_numpy(toks).long().to(t.device)])
+
+
+def oracle_tokens(w, W, x_rows, act, ids, sc, toks, x_scale=None):
+    n = len(toks)
+    return oracle.layer_tokens(W, x_rows, act, n, w.k, w.E, w.n_shared, ids[toks], sc[toks],
+                               np.arange(n, dtype=np.int32), x_scale=x_scale)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_bf16_x_and_h_just_below_4gib():
+    """x [131071, 16384] and h [262142, 8192] in bf16, each 4 GiB - 32 KiB."""
+    w = limit_workload(90, T=131071, H=16384, I=8192)
+    assert w.T * w.H * 2 < LIM <= (w.T + 1) * w.H * 2
+    assert w.R * w.I * 2 < LIM
+    print(f"[limits] bf16 T={w.T} H={w.H} I={w.I} R={w.R}", flush=True)
+    x = wl.make_x_device(w, 0, DEV)
+    logits = wl.make_logits_direct(w)
+    w13, w2, _, _ = wl.make_weights(w, 0, DEV)
+    layer = moe.layer_for_workload(w, DEV)
+    y = layer(x, logits.to(DEV), w13, w2)
+    torch.cuda.synchronize()
+    ids, sc, off, pp = route_and_permute(w, layer, logits)
+    toks = high_tokens(w, off, pp)
+    W = oracle.Weights(host(w13), host(w2), "bf16")
+    ref = oracle_tokens(w, W, rows_of(x, toks), "bf16", ids, sc, toks)
+    err = rel_l2_rows(rows_of(y, toks).double().numpy(), ref)
+    print(f"[limits] bf16: worst token rel L2 {err:.3e} over {len(toks)} tokens", flush=True)
+    assert err < 1e-2
+    del x, w13, w2, layer, y
+    free()
+
+
+def test_fp8_activations_xq_and_hq_just_below_4gib():
+    """fp8 x fp8: xq [262143, 16384] and hq [524286, 8192] e4m3 codes, each
+    4 GiB - 16 KiB (x itself is bf16, 8 GiB)."""
+    w = limit_workload(91, T=262143, H=16384, I=8192, wdt="fp8")
+    assert w.T * w.H < LIM <= (w.T + 1) * w.H
+    assert w.R * w.I < LIM
+    print(f"[limits] fp8 x fp8 T={w.T} H={w.H} I={w.I} R={w.R}", flush=True)
+    x = wl.make_x_device(w, 0, DEV)
+    logits = wl.make_logits_direct(w)
+    w13, w2, s13, s2 = wl.make_weights(w, 0, DEV)
+    layer = moe.layer_for_workload(w, DEV, fp8_act=True)
+    y = layer(x, logits.to(DEV), w13, w2, None, s13, s2)
+    torch.cuda.synchronize()
+    ids, sc, off, pp = route_and_permute(w, layer, logits)
+    toks = high_tokens(w, off, pp)
+    qo, so = oracle.quantize_fp8(rows_of(x, toks).view(torch.int16).numpy(), "bf16")
+    assert np.array_equal(rows_of(layer.xq, toks).view(torch.uint8).numpy(), qo)
+    assert np.array_equal(rows_of(layer.x_scale, toks).numpy(), so)
+    W = oracle.Weights(host(w13), host(w2), "fp8", host(s13), host(s2))
+    ref = oracle_tokens(w, W, qo, "fp8", ids, sc, toks, x_scale=so)
+    err = rel_l2_rows(rows_of(y, toks).double().numpy(), ref)
+    print(f"[limits] fp8 x fp8: worst token rel L2 {err:.3e} over {len(toks)} tokens", flush=True)
+    assert err < 3e-2
+    del x, w13, w2, s13, s2, layer, y
+    free()
+
+
+def test_fused_x_just_below_4gib():
+    """Fused FC1+FC2 with x [131071, 16384] bf16 (4 GiB - 32 KiB), 256 experts
+    of I = 128 plus a shared one: bit-identical to the two-call FFN, and the
+    sampled tokens against the oracle."""
+    w = limit_workload(92, T=131071, H=16384, I=128, E=256)
+    assert w.T * w.H * 2 < LIM <= (w.T + 1) * w.H * 2
+    print(f"[limits] fused T={w.T} H={w.H} I={w.I} E={w.E}", flush=True)
+    x = wl.make_x_device(w, 0, DEV)
+    logits = wl.make_logits_direct(w)
+    w13, w2, _, _ = wl.make_weights(w, 0, DEV)
+    layer = moe.layer_for_workload(w, DEV, fused=True)
+    y = layer(x, logits.to(DEV), w13, w2)
+    torch.cuda.synchronize()
+    ids, sc, off, pp = route_and_permute(w, layer, logits)
+    two_call = moe.expert_ffn(x, layer.offsets, layer.permuted_pair, w13, w2, w.k, w.E, w.n_shared)
+    assert torch.equal(two_call, layer.fc2_out)
+    del two_call
+    toks = high_tokens(w, off, pp)
+    W = oracle.Weights(host(w13), host(w2), "bf16")
+    ref = oracle_tokens(w, W, rows_of(x, toks), "bf16", ids, sc, toks)
+    err = rel_l2_rows(rows_of(y, toks).double().numpy(), ref)
+    print(f"[limits] fused: worst token rel L2 {err:.3e} over {len(toks)} tokens", flush=True)
+    assert err < 1e-2
+    del x, w13, w2, layer, y
+    free()
+
+
+def test_bf16_expert_weights_just_below_4gib():
+    """One expert's w13 [2 x 65408, 16384] bf16: 4 GiB - 8 MiB (128 more
+    intermediate channels would be rejected)."""
+    w = limit_workload(93, T=96, H=16384, I=65408, E=1, n_shared=0)
+    assert 2 * w.I * w.H * 2 < LIM <= 2 * (w.I + 128) * w.H * 2
+    print(f"[limits] weights T={w.T} H={w.H} I={w.I}", flush=True)
+    x = wl.make_x_device(w, 0, DEV)
+    logits = wl.make_logits_direct(w)
+    w13, w2, _, _ = wl.make_weights(w, 0, DEV)
+    layer = moe.layer_for_workload(w, DEV)
+    y = layer(x, logits.to(DEV), w13, w2)
+    torch.cuda.synchronize()
+    ids, sc, off, pp = route_and_permute(w, layer, logits)
+    toks = np.array([0, 1, 47, w.T - 2, w.T - 1], np.int32)
+    W = oracle.Weights(host(w13), host(w2), "bf16")
+    ref = oracle_tokens(w, W, rows_of(x, toks), "bf16", ids, sc, toks)
+    err = rel_l2_rows(rows_of(y, toks).double().numpy(), ref)
+    print(f"[limits] weights: worst token rel L2 {err:.3e} over {len(toks)} tokens", flush=True)
+    assert err < 1e-2
+    del x, w13, w2, layer, y
+    free()
