@@ -179,3 +179,40 @@ def test_bf16_expert_weights_just_below_4gib():
     assert err < 1e-2
     del x, w13, w2, layer, y
     free()
+
+
+@pytest.mark.parametrize("path", ["bf16", "fp8_weights", "fp8_act", "fused", "fused_fp8_weights",
+                                  "fused_fp8_act"])
+def test_most_groups(path):
+    """E = 256 routed experts, top-8 and 64 shared experts: 320 groups, the
+    size of the kernels' group tables; every token against the oracle."""
+    fp8 = "fp8" in path
+    w = wl.Workload("most_groups", 94, T=40, H=256, E=256, I=256, k=8, method=wl.ROUTE_DEEPSEEKV3,
+                    n_group=8, topk_group=4, scaling=2.5, bias=True, n_shared=64,
+                    wdt="fp8" if fp8 else "bf16")
+    assert w.G == 320
+    print(f"[limits] most groups: {path}", flush=True)
+    inp = wl.make_inputs(w, 0)
+    g = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    fp8_act = path in ("fp8_act", "fused_fp8_act")
+    layer = moe.layer_for_workload(w, DEV, fp8_act=fp8_act, fused=path.startswith("fused"))
+    y = layer(g["x"], g["logits"], g["w13"], g["w2"], g["bias"], g["w13_scale"], g["w2_scale"])
+    torch.cuda.synchronize()
+    ids, sc, hard = oracle.route(inp["logits"], w.k, w.method, w.n_group, w.topk_group, inp["bias"],
+                                 w.scaling)
+    assert hard == 0
+    assert np.array_equal(host(layer.ids).numpy(), ids)
+    off, pp, up = oracle.permute(ids, w.E, w.n_shared)
+    assert np.array_equal(host(layer.offsets).numpy(), off)
+    assert np.array_equal(host(layer.permuted_pair).numpy(), pp)
+    toks = np.arange(w.T, dtype=np.int32)
+    W = oracle.Weights(inp["w13"], inp["w2"], w.wdt, inp["w13_scale"], inp["w2_scale"])
+    if fp8_act:
+        qo, so = oracle.quantize_fp8(inp["x"].view(torch.int16).numpy(), "bf16")
+        assert np.array_equal(host(layer.xq).view(torch.uint8).numpy(), qo)
+        ref = oracle.layer_tokens(W, qo, "fp8", w.T, w.k, w.E, w.n_shared, ids, sc, toks, x_scale=so)
+    else:
+        ref = oracle.layer_tokens(W, inp["x"], "bf16", w.T, w.k, w.E, w.n_shared, ids, sc, toks)
+    err = rel_l2_rows(host(y).double().numpy(), ref)
+    print(f"[limits] most groups {path}: worst token rel L2 {err:.3e}", flush=True)
+    assert err < 1e-2
