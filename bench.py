@@ -15,6 +15,8 @@ HBM.  Prints ONE JSON line on stdout (details go to stderr):
   fp8_activations  the fp8 x fp8 path (quantise x in 1x128 blocks, fp8 MFMA
              grouped GEMMs, h quantised in FC1's epilogue) on the same two
              shapes with fp8 e4m3 weights; its rooflines use the fp8 peak
+  routing    moe_route alone for each of the seven routing methods at the
+             prefill and decode T, E and k, against its HBM roofline
   cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
              workload on this host's cores (a reported baseline, not a target)
   calibration  attainable peaks measured in the same run with library kernels
@@ -299,6 +301,57 @@ def time_layer(layer, inp, steps, warmup):
     return ms, {k: round(v[0] / steps, 4) for k, v in kt.items()}
 
 
+ROUTE_METHODS = [(0, "default"), (1, "renormalize"), (2, "deepseek_v3"), (3, "llama4"),
+                 (4, "renormalize_naive"), (5, "minimax2"), (6, "sigmoid_renorm")]
+
+
+def routing_summary(names, device, reps=100):
+    """moe_route alone, every method, at each named workload's T, E and k
+    (DeepSeek-V3's groups and scaling for method 2, a correction bias for 2 and
+    5), against the HBM roofline of one launch: logits (and bias) read once,
+    ids and scales written once.  Logits are N(0, 1) drawn directly."""
+    import torch
+    import mixture_experts_layer_07_amd as moe
+    from mixture_experts_layer_07_amd import workloads as wl
+
+    out = {"kernel": "route_kernel (one launch per call)", "peak_gbps": 8000.0,
+           "logits": "seeded N(0, 1), drawn directly", "reps": reps}
+    for name in names:
+        w = wl.get(name)
+        logits = wl.make_logits_direct(w).to(device)
+        bias = wl.make_bias(w.with_(bias=True)).to(device)
+        ids = torch.empty((w.T, w.k), dtype=torch.int32, device=device)
+        sc = torch.empty((w.T, w.k), dtype=torch.float32, device=device)
+        per = {}
+        for m, mname in ROUTE_METHODS:
+            grouped = m == 2
+            b = bias if m in (2, 5) else None
+
+            def call(m=m, b=b, grouped=grouped):
+                moe.route(logits, w.k, m, w.n_group if grouped else 1,
+                          w.topk_group if grouped else 1, b, w.scaling if grouped else 1.0,
+                          out=(ids, sc))
+
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            moe.timing_enable(True)
+            moe.kernel_times(reset=True)
+            for _ in range(reps):
+                call()
+            torch.cuda.synchronize()
+            ms, n = moe.kernel_times(reset=True)["route"]
+            moe.timing_enable(False)
+            us = ms * 1e3 / n
+            nbytes = w.T * w.E * 4 + (w.E * 4 if b is not None else 0) + w.T * w.k * 8
+            per[mname] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4)}
+        out[name] = {"T": w.T, "E": w.E, "k": w.k, "bytes_per_call": w.T * w.E * 4 + w.T * w.k * 8,
+                     "methods": per}
+        log(f"[bench] routing {name}: " + ", ".join(f"{k} {v['us']} us" for k, v in per.items()))
+    return out
+
+
 def run_workload(name, steps, warmup, device, fp8_act=False, fused=False):
     import torch
     import mixture_experts_layer_07_amd as moe
@@ -413,6 +466,8 @@ def main():
                     help="workloads also run on the fp8-activation path (none: skip)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip timing the fused FC1+FC2 kernel beside each workload")
+    ap.add_argument("--no-routing", action="store_true",
+                    help="skip timing moe_route alone for every routing method")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
@@ -528,6 +583,8 @@ def main():
                     rw, r["touched"], r["fused"], r["per_kernel"], fp8_act=True)
             del r
             torch.cuda.empty_cache()
+    if not args.no_routing:
+        out["routing"] = routing_summary([args.workload, args.decode_workload], dev)
     print(json.dumps(out), flush=True)
 
 
