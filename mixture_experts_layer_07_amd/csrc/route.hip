@@ -14,11 +14,12 @@
 //                      renormalised (DeepSeekV3 with one group, no 1e-20)
 //   SigmoidRenorm      sigmoid, top-k, renormalise
 //
-// Layout: lane l owns experts l, l+64, l+128, l+192 (E <= 256).  Selection
-// keys are packed into one 64-bit integer (order-preserving fp32 bits, then
-// the inverted expert index) so that a single wave-wide max finds the best
-// key with ties going to the lower index; k rounds of that give the ids in
-// selection order.  Group scores and group ranks go through LDS.
+// Layout: lane l owns experts l, l+64, l+128, l+192 (E <= 256).  Each of the
+// k selection rounds takes the wave maximum of the order-preserving fp32 key
+// bits (DPP steps within the wave, no LDS round trips), then the lowest expert
+// index holding that key from four ballots (index = 64 * slot + lane, slots
+// checked in order); k rounds give the ids in selection order.  Group scores
+// and group ranks go through LDS.
 #include <math.h>
 
 #include "common.h"
@@ -40,19 +41,27 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t u)
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-__device__ __forceinline__ uint64_t pack_key(float v, int e)
+// max(v, v of the lane that DPP control `ctrl` names); rows outside
+// `row_mask` and lanes without a source keep v
+template <int ctrl, int row_mask>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v)
 {
-    return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, row_mask, 0xf, false);
+    return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// Maximum over the 64 lanes (all active), the same in every lane: pairs and
+// quads, half-rows and rows of 16 by lane permutations, then rows 0..3
+// folded into lane 63 by the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141, 0xf>(v);  // row_half_mirror
+    v = dpp_max<0x140, 0xf>(v);  // row_mirror
+    v = dpp_max<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v)
@@ -156,9 +165,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     if (!active) return;  // no block-wide barrier below this point
 
-    uint64_t cand[4];
+    uint32_t kb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cand[i] = valid[i] ? pack_key(key[i], lane + 64 * i) : 0ull;
+    for (int i = 0; i < 4; ++i) kb[i] = ordered_bits(key[i]);
 
     int sel_id[MOE_MAX_TOPK];
     float sel_key[MOE_MAX_TOPK];
@@ -167,17 +176,23 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         sel_id[j] = 0;
         sel_key[j] = 0.0f;
         if (j < k) {
-            uint64_t best = cand[0];
+            // invalid candidates enter the maximum as 0, at or below every
+            // valid key, and never win a ballot
+            uint32_t m = 0;
 #pragma unroll
-            for (int i = 1; i < 4; ++i) best = cand[i] > best ? cand[i] : best;
-            best = wave_max_u64(best);
-            int e = (int)(0xffffffffu - (uint32_t)best);
-            e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+            for (int i = 0; i < 4; ++i) m = (valid[i] && kb[i] > m) ? kb[i] : m;
+            m = wave_max_u32(m);
+            int e = 0;  // no valid candidate left: expert 0 (cannot happen after validation)
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                const uint64_t b = __ballot(valid[i] && kb[i] == m);
+                if (b) e = 64 * i + __ffsll((unsigned long long)b) - 1;
+            }
             sel_id[j] = e;
-            sel_key[j] = from_ordered_bits((uint32_t)(best >> 32));
+            sel_key[j] = from_ordered_bits(m);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (cand[i] == best) cand[i] = 0ull;
+                if (64 * i + lane == e) valid[i] = false;
         }
     }
 
