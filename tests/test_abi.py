@@ -200,3 +200,4 @@ def test_binding_rejects_tensors_on_another_device(L):
     import torch
     with pytest.raises(ValueError, match="moe_finalize: a tensor on cpu, expected cuda:0"):
         binding._call("moe_finalize", "cuda:0", torch.zeros(8), 0, None, None, 1, 1, 8, 0, None, 0)
+
