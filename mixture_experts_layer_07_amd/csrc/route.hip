@@ -72,6 +72,30 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return v;
 }
 
+// (a1 >= a2) := the two largest of (a1, a2) and the pair held by the lane
+// that DPP control `ctrl` names (all lanes active; no NaN in either pair).
+template <int ctrl>
+__device__ __forceinline__ void dpp_top2(float& a1, float& a2)
+{
+    const float c1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(a1), __float_as_int(a1),
+                                                                ctrl, 0xf, 0xf, false));
+    const float c2 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(a2), __float_as_int(a2),
+                                                                ctrl, 0xf, 0xf, false));
+    const float lo = c1 > a1 ? a1 : c1;
+    const float hi2 = c2 > a2 ? c2 : a2;
+    a1 = c1 > a1 ? c1 : a1;
+    a2 = lo > hi2 ? lo : hi2;
+}
+
+// Running top-2 of a group's keys (selects, not branches, so that the pair
+// stays in registers); NaN keys never enter.
+__device__ __forceinline__ void top2_add(float v, float& b1, float& b2)
+{
+    const bool above1 = v > b1, above2 = v > b2;
+    b2 = above1 ? b1 : (above2 ? v : b2);
+    b1 = above1 ? v : b1;
+}
+
 // fl32 of the fp64 sigmoid: the fp32 key both sides of a parity check agree on.
 __device__ __forceinline__ float sigmoid_key(float l)
 {
@@ -127,20 +151,30 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     if (dsv3) {
         const int gsz = E / n_group;
         __syncthreads();
-        // group score: sum of the two largest biased keys of the group
-        if (active) {
+        // group score: sum of the two largest biased keys of the group (one
+        // fp32 add of the same two values whichever lanes find them).  With
+        // n_group a power of two and at most 16 lanes per group, the group's
+        // `parts` consecutive lanes each scan a slice and merge their top-2
+        // pairs by DPP steps within aligned blocks of 2, 4, 8, 16 lanes;
+        // otherwise one lane scans each group.
+        const int parts = n_group <= 64 ? 64 / n_group : 0;
+        const bool split = parts >= 1 && parts <= 16 && (n_group & (n_group - 1)) == 0 &&
+                           gsz % parts == 0;
+        if (active && split) {
+            const int g = lane / parts, len = gsz / parts;
+            const float* src = &s_key[wave][g * gsz + (lane % parts) * len];
+            float b1 = -INFINITY, b2 = -INFINITY;
+            for (int i = 0; i < len; ++i) top2_add(src[i], b1, b2);
+            if (parts >= 2) dpp_top2<0xb1>(b1, b2);   // quad_perm [1,0,3,2]
+            if (parts >= 4) dpp_top2<0x4e>(b1, b2);   // quad_perm [2,3,0,1]
+            if (parts >= 8) dpp_top2<0x141>(b1, b2);  // row_half_mirror
+            if (parts >= 16) dpp_top2<0x140>(b1, b2); // row_mirror
+            if (lane % parts == 0) s_gs[wave][g] = b1 + b2;
+        } else if (active) {
             for (int g = lane; g < n_group; g += 64) {
                 float b1 = -INFINITY, b2 = -INFINITY;
-                for (int i = 0; i < gsz; ++i) {
-                    const float v = s_key[wave][g * gsz + i];
-                    if (v > b1) {
-                        b2 = b1;
-                        b1 = v;
-                    } else if (v > b2) {
-                        b2 = v;
-                    }
-                }
-                s_gs[wave][g] = b1 + b2;  // one fp32 add
+                for (int i = 0; i < gsz; ++i) top2_add(s_key[wave][g * gsz + i], b1, b2);
+                s_gs[wave][g] = b1 + b2;
             }
         }
         __syncthreads();

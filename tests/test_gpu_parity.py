@@ -77,6 +77,7 @@ TIE_GRID = np.array([-2, -1, 0, 1, 2], np.float32) / np.float32(4)
     (8, 2, 0, 1, 1), (8, 8, 0, 1, 1), (64, 6, 1, 1, 1), (65, 3, 4, 1, 1), (256, 8, 4, 1, 1),
     (128, 8, 0, 1, 1), (256, 8, 2, 8, 4), (256, 1, 2, 8, 1), (64, 8, 2, 32, 4),
     (256, 8, 2, 128, 8), (96, 5, 2, 3, 2), (12, 4, 2, 6, 3), (256, 8, 2, 16, 16),
+    (256, 8, 2, 4, 2), (64, 4, 2, 2, 1), (48, 4, 2, 8, 3),
     (8, 1, 3, 1, 1), (128, 4, 3, 1, 1), (64, 8, 5, 1, 1), (256, 8, 5, 1, 1),
     (32, 4, 6, 1, 1), (256, 8, 6, 1, 1), (7, 7, 6, 1, 1),
 ])
