@@ -105,10 +105,22 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t* __re
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int p0 = blockIdx.x * kChunk;
     const int p1 = min(P, p0 + kChunk);
-    for (int pb = p0; pb < p1; pb += 64) {
-        const int p = pb + lane;
+    // the chunk's ids, all loads in flight at once (one memory latency per
+    // chunk instead of one per 64 pairs)
+    constexpr int kIter = kChunk / 64;
+    static_assert(kChunk % 64 == 0, "whole waves per chunk");
+    int idv[kIter];
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+        const int p = p0 + it * 64 + lane;
+        idv[it] = p < p1 ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+        if (p0 + it * 64 >= p1) break;  // past the last pair (wave-uniform)
+        const int p = p0 + it * 64 + lane;
         const bool valid = p < p1;
-        const int e = valid ? clamp_id(ids[p], E) : 0;
+        const int e = valid ? clamp_id(idv[it], E) : 0;
         uint64_t peers = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (e >> b) & 1;
