@@ -408,6 +408,39 @@ def test_kernel_timing_hooks():
         assert t[name][1] >= 3 and t[name][1] % 3 == 0 and t[name][0] > 0, (name, t[name])
 
 
+def test_kernel_timing_collected_while_launching():
+    """Reading and resetting the kernel times from one thread while another
+    launches timed calls: every launch is counted exactly once, each with
+    both of its events recorded."""
+    import threading
+    logits = torch.randn(512, 64, generator=torch.Generator().manual_seed(7)).to(DEV)
+    n_calls, totals, errors = 400, [0], []
+    done = threading.Event()
+
+    def collect():
+        try:
+            while not done.is_set():
+                totals[0] += moe.kernel_times(reset=True)["route"][1]
+        except Exception as exc:  # reported by the main thread
+            errors.append(exc)
+
+    moe.timing_enable(True)
+    try:
+        moe.kernel_times(reset=True)
+        reader = threading.Thread(target=collect)
+        reader.start()
+        for _ in range(n_calls):
+            moe.route(logits, 4, 0)
+        torch.cuda.synchronize()
+        done.set()
+        reader.join()
+        last = moe.kernel_times(reset=True)["route"]
+    finally:
+        moe.timing_enable(False)
+    assert not errors, errors
+    assert totals[0] + last[1] == n_calls
+
+
 def test_shared_expert_as_separate_call_on_second_stream():
     """The shared expert run as its own expert_ffn call (one group over all
     tokens, identity rows, writing fc2_out rows P..P+T) on a second stream,
