@@ -291,17 +291,27 @@ moe_status moe_expert_ffn_fp8_fused(const uint8_t* xq, const float* x_scale, int
 
 /* Bytes of workspace that moe_permute and moe_expert_ffn need for this shape
  * (0 on invalid arguments).  One buffer of this size serves both calls.
- * act = MOE_FP8_E4M3 sizes it for moe_expert_ffn_fp8. */
+ * act = MOE_FP8_E4M3 sizes it for moe_expert_ffn_fp8.  The size depends only
+ * on the shape (T*k rows, never on how tokens are routed), so a caller can
+ * allocate it once, up front, and reuse it on every call: the gsyq.cn
+ * article's remedy for allocator fragmentation in grouped-GEMM MoE layers
+ * (section 4.4, "显存碎片导致的 OOM").  Host-only; never fails otherwise. */
 size_t moe_workspace_size(int T, int k, int E, int n_shared, int H, int I, int act);
 
-/* Static description of a status code. */
+/* Static, never-NULL description of a status code (unknown codes included).
+ * Part of reporting unsupported requests loudly instead of degrading
+ * silently (TensorRT-LLM page, section "融合算子与回退阈值"). */
 const char* moe_status_string(int status);
 
-/* Reason for the last non-OK status returned on the calling thread. */
+/* Reason for the last non-OK status returned on the calling thread (a
+ * thread-local, NUL-terminated string owned by the library, valid until that
+ * thread's next call; "" before any failure): the message that names the
+ * limit an unsupported shape exceeds (same section as above). */
 const char* moe_last_error(void);
 
 /*
- * Per-kernel timing (measurement support, off by default).  When enabled,
+ * Per-kernel timing (measurement support for the benchmark, not a step of the
+ * layer; off by default).  When enabled,
  * every launch is bracketed by two HIP events recorded on the launch stream;
  * moe_kernel_times() waits for the recorded events and returns, per kernel
  * id, the summed milliseconds and the launch count since the last reset.

@@ -9,15 +9,19 @@
 // w2 [G, H, I] as on the vLLM page ("专家权重如何存储"); gated FC1 with 2*I
 // outputs as on the TensorRT-LLM page ("权重加载").
 //
-// Scheduling.  One launch covers every group: the work list is the flattened
-// set of (group, N-tile, M-tile) triples ("从 Dense GEMM 到 TP MoE 的演进逻辑",
-// section 2.2: tile scheduling over all groups beats one block per group when
-// row counts are uneven).  Each workgroup derives the list from the offsets on
-// the device (no host read-back), so the launch is graph-capturable.  The grid
-// is persistent (sized by CU count and occupancy); workgroups stride through
-// the list with an XCD-aware mapping: workgroup b runs on XCD b % 8, and in
-// each round XCD x takes one contiguous slice of the list, so the M-tiles that
-// share a weight tile run together on the same XCD and share its L2.
+// Scheduling.  Work is a flattened list of (group, N-tile, M-tile) triples
+// ("从 Dense GEMM 到 TP MoE 的演进逻辑", section 2.2: tile scheduling over all
+// groups beats one block per group when row counts are uneven).  Groups are
+// split by row count into three classes (skinny, mid, big), and each GEMM is
+// issued as one launch per class, back to back on the caller's stream, each
+// with the tile shape that suits its class (run_classes_dma below); a launch's
+// list holds the tiles of its class's groups only.  Each workgroup derives its
+// launch's list from the offsets on the device (no host read-back), so the
+// launches are graph-capturable.  The grid is persistent (sized by CU count
+// and occupancy); workgroups stride through the list with an XCD-aware
+// mapping: workgroup b runs on XCD b % 8, and in each round XCD x takes one
+// contiguous slice of the list, so the M-tiles that share a weight tile run
+// together on the same XCD and share its L2.
 //
 // Two tile engines.  Both operands are K-contiguous (activation rows and
 // weight rows), staged through LDS in 128-byte K slices whose 16-byte chunks

@@ -147,6 +147,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                 s_key[wave][e] = key[i];
             }
         }
+        if (!dsv3) {
+            // The weights below read s_sig entries that other lanes of this
+            // wave stored (DeepSeek-V3 reaches them through __syncthreads).
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        }
     }
     if (dsv3) {
         const int gsz = E / n_group;
