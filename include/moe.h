@@ -84,6 +84,9 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype
 /* Largest intermediate size of the fused FC1+FC2 kernels (h of a 16-row tile
  * is kept in LDS). */
 #define MOE_FUSED_MAX_I 2048
+/* Bytes of the library's static device scratch used by moe_expert_ffn_noalloc
+ * (64 MiB per GPU the library runs on, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * moe_route -- per-token expert selection and weights.
@@ -179,6 +182,27 @@ moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, in
                           const int32_t* permuted_pair, const void* w13, const void* w2,
                           int wdt, const float* w13_scale, const float* w2_scale,
                           void* fc2_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_noalloc -- moe_expert_ffn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): same arguments minus the workspace, same kernels and
+ * bit-identical results.  h lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES instead; a shape whose h, (T*k + n_shared*T) * I
+ * activation values, does not fit returns MOE_ERR_UNSUPPORTED before anything
+ * is launched.  Nothing is allocated: no hipMalloc, no hipFree (the scratch's
+ * device address is looked up once per GPU, on the first call there).  h is
+ * written before it is read, so nothing is cleared between calls.  Every call
+ * on one GPU shares that GPU's scratch, which keeps the last call's contents:
+ * calls that overlap on one GPU (two streams, two threads) race.  With
+ * moe_timing_enable on, the timing hooks create HIP events; keep timing off
+ * where nothing may be allocated.
+ */
+moe_status moe_expert_ffn_noalloc(const void* x, int act, int T, int H, int I, int k, int E,
+                                  int n_shared, const int32_t* expert_offsets,
+                                  const int32_t* permuted_pair, const void* w13, const void* w2,
+                                  int wdt, const float* w13_scale, const float* w2_scale,
+                                  void* fc2_out, void* stream);
 
 /*
  * moe_finalize -- y_t = sum_j scales[t,j] * fc2_out[unpermute[t*k+j]]

@@ -23,6 +23,7 @@ ROUTE_FLAG_RENORMALIZE = 1
 KERNEL_IDS = ["route", "permute_count", "permute_scan", "permute_scatter", "fc1", "fc2",
               "finalize", "quantize", "ffn_fused"]
 FUSED_MAX_I = 2048
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 _lib = None
@@ -49,6 +50,7 @@ def lib():
         L.moe_finalize.argtypes = [P, i, P, P, i, i, i, i, P, i, P]
         L.moe_quantize_fp8.argtypes = [P, i, i, i, P, P, P]
         L.moe_expert_ffn_fp8.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P, P, P, P, z, P]
+        L.moe_expert_ffn_noalloc.argtypes = [P, i, i, i, i, i, i, i, P, P, P, P, i, P, P, P, P]
         L.moe_expert_ffn_fused.argtypes = [P, i, i, i, i, i, i, i, P, P, P, P, i, P, P, i, P, P]
         L.moe_expert_ffn_fp8_fused.argtypes = [P, P, i, i, i, i, i, i, P, P, P, P, P, P, i, P, P]
         L.moe_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -59,7 +61,7 @@ def lib():
         L.moe_last_error.restype = C.c_char_p
         L.moe_timing_enable.argtypes = [i]
         L.moe_kernel_times.argtypes = [P, P, i]
-        for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_finalize",
+        for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_finalize",
                    "moe_quantize_fp8", "moe_expert_ffn_fp8", "moe_expert_ffn_fused",
                    "moe_expert_ffn_fp8_fused", "moe_timing_enable",
                    "moe_kernel_times"):
@@ -199,6 +201,32 @@ def expert_ffn(x, expert_offsets, permuted_pair, w13, w2, k, E, n_shared=0, w13_
     _dev(ws, "ws", torch.uint8)
     _call("moe_expert_ffn", x.device, x, _DT[x.dtype], T, H, I, k, E, n_shared, expert_offsets,
           permuted_pair, w13, w2, _DT[w13.dtype], w13_scale, w2_scale, out, ws, ws.numel())
+    return out
+
+
+def expert_ffn_noalloc(x, expert_offsets, permuted_pair, w13, w2, k, E, n_shared=0,
+                       w13_scale=None, w2_scale=None, out=None):
+    """moe_expert_ffn_noalloc: expert_ffn with h in the library's static device
+    scratch (no workspace; MOE_NOALLOC_SCRATCH_BYTES bounds h) -> fc2_out."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    T, H = x.shape
+    G = E + n_shared
+    _dev(w13, "w13", (torch.float32, torch.bfloat16, torch.float8_e4m3fn))
+    I = w13.shape[1] // 2
+    _dev(w13, "w13", shape=(G, 2 * I, H))
+    _dev(w2, "w2", w13.dtype, (G, H, I))
+    _dev(expert_offsets, "expert_offsets", torch.int32, (G + 1,))
+    _dev(permuted_pair, "permuted_pair", torch.int32, (T * k,))
+    if w13.dtype == torch.float8_e4m3fn:
+        _dev(w13_scale, "w13_scale", torch.float32, (G, 2 * I // 128, H // 128))
+        _dev(w2_scale, "w2_scale", torch.float32, (G, H // 128, I // 128))
+    R = T * k + n_shared * T
+    if out is None:
+        out = torch.empty((R, H), dtype=x.dtype, device=x.device)
+    else:
+        _dev(out, "fc2_out", x.dtype, (R, H))
+    _call("moe_expert_ffn_noalloc", x.device, x, _DT[x.dtype], T, H, I, k, E, n_shared,
+          expert_offsets, permuted_pair, w13, w2, _DT[w13.dtype], w13_scale, w2_scale, out)
     return out
 
 

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "fused.hip", "finalize.hip",
-           "quant.hip"]
+           "quant.hip", "noalloc.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

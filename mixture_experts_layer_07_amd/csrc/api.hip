@@ -215,11 +215,12 @@ moe_status moe_permute(const int32_t* ids, int T, int k, int E, int n_shared,
                           static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, int E,
-                          int n_shared, const int32_t* expert_offsets,
-                          const int32_t* permuted_pair, const void* w13, const void* w2,
-                          int wdt, const float* w13_scale, const float* w2_scale,
-                          void* fc2_out, void* ws, size_t ws_bytes, void* stream)
+// Host checks of moe_expert_ffn and moe_expert_ffn_noalloc (everything but
+// the workspace).
+static moe_status check_ffn(const void* x, int act, int T, int H, int I, int k, int E, int n_shared,
+                            const int32_t* expert_offsets, const int32_t* permuted_pair,
+                            const void* w13, const void* w2, int wdt, const float* w13_scale,
+                            const float* w2_scale, void* fc2_out)
 {
     moe_status st = check_common(T, k, E, n_shared);
     if (st != MOE_OK) return st;
@@ -240,9 +241,43 @@ moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, in
     if (T == 0) return MOE_OK;
     if (!x || !expert_offsets || !w13 || !w2 || !fc2_out || (E > 0 && !permuted_pair))
         return set_error(MOE_ERR_INVALID_ARG, "x, expert_offsets, permuted_pair, w13, w2 and fc2_out must be non-null");
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const void* x, int act, int T, int H, int I, int k, int E,
+                          int n_shared, const int32_t* expert_offsets,
+                          const int32_t* permuted_pair, const void* w13, const void* w2,
+                          int wdt, const float* w13_scale, const float* w2_scale,
+                          void* fc2_out, void* ws, size_t ws_bytes, void* stream)
+{
+    moe_status st = check_ffn(x, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2,
+                              wdt, w13_scale, w2_scale, fc2_out);
+    if (st != MOE_OK || T == 0) return st;
     const size_t need = ffn_scratch_bytes(T, k, n_shared, I, act);
     if (!ws || ws_bytes < need)
         return set_error(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes (got %zu)", need, ws_bytes);
+    return launch_ffn(x, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2, wdt,
+                      wdt == MOE_FP8_E4M3 ? w13_scale : nullptr,
+                      wdt == MOE_FP8_E4M3 ? w2_scale : nullptr, fc2_out, ws,
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_ffn_noalloc(const void* x, int act, int T, int H, int I, int k, int E,
+                                  int n_shared, const int32_t* expert_offsets,
+                                  const int32_t* permuted_pair, const void* w13, const void* w2,
+                                  int wdt, const float* w13_scale, const float* w2_scale,
+                                  void* fc2_out, void* stream)
+{
+    moe_status st = check_ffn(x, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2,
+                              wdt, w13_scale, w2_scale, fc2_out);
+    if (st != MOE_OK || T == 0) return st;
+    const size_t need = ffn_scratch_bytes(T, k, n_shared, I, act);
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return set_error(MOE_ERR_UNSUPPORTED,
+                         "expert_ffn_noalloc: h needs %zu bytes, the static scratch holds %zu "
+                         "(use moe_expert_ffn with a workspace)", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = noalloc_scratch();
+    if (!ws) return MOE_ERR_DEVICE;
     return launch_ffn(x, act, T, H, I, k, E, n_shared, expert_offsets, permuted_pair, w13, w2, wdt,
                       wdt == MOE_FP8_E4M3 ? w13_scale : nullptr,
                       wdt == MOE_FP8_E4M3 ? w2_scale : nullptr, fc2_out, ws,

@@ -133,6 +133,10 @@ moe_status launch_ffn_fused(const void* x, const float* x_scale, int act, int T,
                             int E, int n_shared, const int32_t* offsets, const int32_t* permuted_pair,
                             const void* w13, const void* w2, int wdt, const float* w13_scale,
                             const float* w2_scale, int split, void* fc2_out, hipStream_t s);
+// Device address of this GPU's copy of the static scratch behind
+// moe_expert_ffn_noalloc (MOE_NOALLOC_SCRATCH_BYTES), resolved once per
+// device; null with the error set if the lookup fails.
+void* noalloc_scratch();
 moe_status launch_quantize_fp8(const void* x, int dt, int rows, int cols, uint8_t* q, float* scale,
                                hipStream_t s);
 moe_status launch_finalize(const void* fc2_out, int dt, const int32_t* unpermute,

@@ -104,6 +104,22 @@ def test_expert_ffn_validation(L):
     assert "4 GiB" in err(L)
 
 
+def test_expert_ffn_noalloc_validation(L):
+    """Same host checks as moe_expert_ffn (no workspace), plus the static
+    scratch's size limit for h, all before anything touches the device."""
+    p = C.c_void_p(16)
+    f = lambda T, H, I, wdt=1, s13=p, s2=p, x=p: L.moe_expert_ffn_noalloc(  # noqa: E731
+        x, 1, T, H, I, 8, 256, 1, p, p, p, p, wdt, s13, s2, p, None)
+    assert f(16, 100, 128) == UNSUPPORTED                 # H % 128
+    assert f(16, 128, 128, wdt=2, s13=None) == INVALID    # fp8 weights need scales
+    assert f(16, 128, 128, x=None) == INVALID             # null x
+    assert f(0, 128, 128, x=None) == OK                   # T = 0: nothing launched
+    # h = (T*k + n_shared*T) * I bf16 values: 64 MiB holds 1820 tokens at k = 8 + 1 shared, I = 2048
+    lim = binding.NOALLOC_SCRATCH_BYTES // (9 * 2048 * 2)
+    assert f(lim + 1, 7168, 2048) == UNSUPPORTED
+    assert "static scratch" in err(L)
+
+
 def test_quantize_fp8_validation(L):
     p = C.c_void_p(16)
     q = L.moe_quantize_fp8
