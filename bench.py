@@ -11,19 +11,24 @@ HBM.  Prints ONE JSON line on stdout (details go to stderr):
              per launch / its mean launch duration from HIP events recorded on
              the launch stream, over as many steps again as were timed (the
              timed steps themselves run without the events)
-  decode     the same figures for the DeepSeek-V3-shaped decode batch (T=512)
+  workloads  every configuration (tiny fp32, Mixtral-shaped bf16, DeepSeek-V3
+             decode and prefill, Qwen3-shaped fp8 weights): tokens/s, ms per
+             step, FC1 and FC2 rooflines, the grouped-GEMM summary and a
+             cpu_baseline of its own
   fp8_activations  the fp8 x fp8 path (quantise x in 1x128 blocks, fp8 MFMA
-             grouped GEMMs, h quantised in FC1's epilogue) on the same two
-             shapes with fp8 e4m3 weights; its rooflines use the fp8 peak
+             grouped GEMMs, h quantised in FC1's epilogue) on the two
+             DeepSeek-V3 shapes with fp8 e4m3 weights; rooflines use the fp8 peak
   routing    moe_route alone for each of the seven routing methods at the
              prefill and decode T, E and k, against its HBM roofline
   cpu_baseline  the CPU oracle timed on a bounded token sample of the headline
              workload on this host's cores (a reported baseline, not a target)
-  calibration  attainable peaks measured in the same run with library kernels
-             (a 1 GiB device copy; 8192^3 bf16 and fp8 GEMMs of torch/hipBLASLt
-             on random data); each roofline also reports its fraction of these
+  calibration  attainable peaks measured in the same run: an HBM read stream
+             (the repository's own kernel, non-temporal 16-byte loads over
+             4 GiB), a 1 GiB device copy, and 8192^3 bf16 / fp8 GEMMs of
+             torch/hipBLASLt on random data; each roofline also reports its
+             fraction of these
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads ...]
 """
 import argparse
 import hashlib
@@ -84,6 +89,19 @@ def fc_work(w, touched_groups, which, fp8_act=False):
     return flops, nbytes
 
 
+def fc_min_bytes(w, touched_groups, which, fp8_act=False):
+    """The method's minimum traffic attributed to one GEMM: the touched groups'
+    weights plus x read once (FC1) or y written once (FC2); h and fc2_out,
+    which this two-kernel design also moves, are not counted."""
+    wsz = {"f32": 4, "bf16": 2, "fp8": 1}[w.wdt]
+    asz = 4 if w.act == "f32" else 2
+    sc = 4.0 / (128 * 128) if w.wdt == "fp8" else 0.0
+    if which == "fc1":
+        qsz = 1 + 4.0 / 128 if fp8_act else asz
+        return touched_groups * 2 * w.I * w.H * (wsz + sc) + w.T * w.H * qsz
+    return touched_groups * w.H * w.I * (wsz + sc) + w.T * w.H * asz
+
+
 def mfma_peak(w, fp8_act=False):
     return PEAK["fp8" if fp8_act else ("f32" if w.act == "f32" else "bf16")]
 
@@ -101,13 +119,19 @@ def roofline(w, touched, ms_per_step, which=DOMINANT, traffic=None, launches=Non
         ach, peak, unit, bound = flops / s / 1e12, peak_f, "TFLOP/s", "mfma"
     else:
         ach, peak, unit, bound = nbytes / s / 1e9, PEAK["hbm"], "GB/s", "hbm"
+    nmin = fc_min_bytes(w, touched, which, fp8_act)
     return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
             "frac": round(ach / peak, 4), "traffic": traffic,
             "kernel": f"grouped GEMM {which.upper()} (row-class launches per step: {launches})",
             "ms_per_step": round(ms_per_step, 4),
             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
             "mfma_frac": round(flops / s / 1e12 / peak_f, 4),
-            "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4)}
+            "hbm_frac": round(nbytes / s / 1e9 / PEAK["hbm"], 4),
+            "algorithmic_bytes_min": nmin,
+            "hbm_frac_min": round(nmin / s / 1e9 / PEAK["hbm"], 4),
+            "bytes_note": ("algorithmic_bytes: touched weights + the GEMM's activation input "
+                           "(x or h) + its output (h or fc2_out); algorithmic_bytes_min: touched "
+                           "weights + x (FC1) or y (FC2) only, the method's minimum")}
 
 
 def fused_summary(w, touched, res, two_call_kernels, fp8_act=False):
@@ -152,10 +176,11 @@ def grouped_gemm_summary(w, touched, per_kernel, fp8_act=False):
             "hbm_frac": round((b1 + b2) / s / 1e9 / PEAK["hbm"], 4)}
 
 
-def load_traffic(workload):
-    """HBM bytes per FC1 launch from the committed rocprofv3 counter summary,
-    or None when the summary is missing or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
+def load_traffic(workload, which="fc1"):
+    """HBM bytes per step of one grouped GEMM (all its row-class launches) from
+    the committed rocprofv3 counter summary, or None when the summary is
+    missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{which}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -190,6 +215,7 @@ def calibrate(device, reps=5):
 
     out["hbm_copy_gbps"] = round(2 * src.numel() / best(lambda: dst.copy_(src)) / 1e9, 1)
     del src, dst
+    out["hbm_read_gbps"] = hbm_read_stream(device, best)
     n = 8192
     a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
@@ -205,9 +231,37 @@ def calibrate(device, reps=5):
         log(f"[bench] fp8 calibration GEMM unavailable: {type(e).__name__}: {e}")
     del a, b
     torch.cuda.empty_cache()
-    out["method"] = ("best of 5: torch copy_ of 1 GiB (2 GiB moved), torch.matmul bf16 8192^3, "
-                     "torch._scaled_mm e4m3 8192^3 (unit scales), N(0,1) operands")
+    out["method"] = ("best of 5: HBM read stream of 4 GiB (libmoe_calib: non-temporal 16-byte "
+                     "loads, 1-4 workgroups of 1024 threads per CU, best), torch copy_ of 1 GiB "
+                     "(2 GiB moved), torch.matmul bf16 8192^3, torch._scaled_mm e4m3 8192^3 "
+                     "(unit scales), N(0,1) operands")
     return out
+
+
+def hbm_read_stream(device, best):
+    """GB/s of reading a 4 GiB device buffer once (the repository's stream
+    kernel, libmoe_calib.so), best over 1, 2 and 4 workgroups per CU."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "mixture_experts_layer_07_amd", "libmoe_calib.so")
+    L = ctypes.CDLL(path)
+    L.moe_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    L.moe_calib_stream_read.restype = ctypes.c_int
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device).random_()
+    ncu = torch.cuda.get_device_properties(device).multi_processor_count
+    out = torch.empty(4 * ncu * 1024, dtype=torch.int32, device=device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    rate = 0.0
+    for per_cu in (1, 2, 4):
+        def run(g=per_cu * ncu):
+            rc = L.moe_calib_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), g, stream)
+            if rc != 0:
+                raise RuntimeError(f"moe_calib_stream_read failed: hipError {rc}")
+        rate = max(rate, nbytes / best(run) / 1e9)
+    del buf, out
+    return round(rate, 1)
 
 
 def add_calibrated(rl, cal, fp8_act=False):
@@ -215,7 +269,7 @@ def add_calibrated(rl, cal, fp8_act=False):
     if cal is None:
         return rl
     if rl["bound"] == "hbm":
-        peak = cal.get("hbm_copy_gbps")
+        peak = cal.get("hbm_read_gbps")
     else:
         peak = cal.get("fp8_gemm_tflops" if fp8_act else "bf16_gemm_tflops")
     rl["calibrated_peak"] = peak
@@ -236,41 +290,50 @@ def calibration_copy(mib, device):
 
 
 def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
-    """Write profiles/fc1_<workload>_traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --calibrate-copy-mib N --no-decode --no-cpu-baseline` (FETCH_SIZE,
-    then WRITE_SIZE; counter values are KiB per dispatch).  FC1's HBM bytes per
-    step are the counters summed over its row-class launches, divided by the
-    number of layer calls, each scaled by true/counted bytes of the copy."""
+    """Write profiles/fc1_<workload>_traffic.json and fc2_<workload>_traffic.json
+    from two rocprofv3 --pmc runs of `bench.py --workloads <workload>
+    --calibrate-copy-mib N ...` (FETCH_SIZE, then WRITE_SIZE; counter values are
+    KiB per dispatch).  A GEMM's HBM bytes per step are its counters summed over
+    its row-class launches, divided by the number of layer calls, each scaled by
+    true/counted bytes of the copy."""
     import csv
 
-    def load(d, counter):
+    def rows_of(d, counter):
         path = os.path.join(d, "run_counter_collection.csv")
         if not os.path.exists(path):
             for root, _, files in os.walk(d):
                 for f in files:
                     if f.endswith("counter_collection.csv"):
                         path = os.path.join(root, f)
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        return path, [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+    def is_gemm(name, mode):
+        return (f"dma_gemm_kernel<{mode}," in name
+                or ("grouped_gemm_kernel<" in name and f", {mode}, moe::" in name))
+
+    def load(d, counter, mode):
+        path, rows = rows_of(d, counter)
         calib = [float(r["Counter_Value"]) for r in rows if "bitwise_not" in r["Kernel_Name"]]
-        fc1 = [float(r["Counter_Value"]) for r in rows
-               if ("dma_gemm_kernel<0," in r["Kernel_Name"]
-                   or ("grouped_gemm_kernel<" in r["Kernel_Name"] and ", 0, moe::" in r["Kernel_Name"]))]
+        vals = [float(r["Counter_Value"]) for r in rows if is_gemm(r["Kernel_Name"], mode)]
         calls = sum(1 for r in rows if "route_kernel" in r["Kernel_Name"])
-        if not calib or not fc1 or not calls:
-            raise SystemExit(f"{path}: calibration copy, FC1 or route dispatches missing")
+        if not calib or not vals or not calls:
+            raise SystemExit(f"{path}: calibration copy, GEMM or route dispatches missing")
         scale = (copy_mib * 1024.0) / max(calib)
-        return sum(fc1) * 1024.0 * scale / calls, scale, calls
-    fetch, sf, n1 = load(fetch_dir, "FETCH_SIZE")
-    write, sw, n2 = load(write_dir, "WRITE_SIZE")
-    out = {"workload": workload, "kernel": "grouped GEMM FC1 (all row-class launches of a step)",
-           "kernel_source_sha": kernel_sha(), "fetch_bytes_per_launch": fetch,
-           "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
-           "copy_calibration": {"mib": copy_mib, "fetch_scale": sf, "write_scale": sw},
-           "layer_calls_seen": [n1, n2], "commands": commands}
-    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+        return sum(vals) * 1024.0 * scale / calls, scale, calls
+
+    for mode, which in ((0, "fc1"), (1, "fc2")):
+        fetch, sf, n1 = load(fetch_dir, "FETCH_SIZE", mode)
+        write, sw, n2 = load(write_dir, "WRITE_SIZE", mode)
+        out = {"workload": workload,
+               "kernel": f"grouped GEMM {which.upper()} (all row-class launches of a step)",
+               "kernel_source_sha": kernel_sha(), "fetch_bytes_per_launch": fetch,
+               "write_bytes_per_launch": write, "hbm_bytes_per_launch": fetch + write,
+               "copy_calibration": {"mib": copy_mib, "fetch_scale": sf, "write_scale": sw},
+               "layer_calls_seen": [n1, n2], "commands": commands}
+        path = os.path.join(ROOT, "profiles", f"{which}_{workload}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out, indent=1))
 
 
 def time_layer(layer, inp, steps, warmup):
@@ -454,24 +517,55 @@ def cpu_baseline(res, seconds):
                        f"scaled to {w.T} tokens; fp64, OpenMP over tokens")}
 
 
+WORKLOAD_ORDER = ["dsv3_prefill", "dsv3_decode", "tiny_fp32", "mixtral_bf16", "qwen3_fp8"]
+
+
+def describe(w):
+    return (f"{w.name}: T={w.T} H={w.H} E={w.E}+{w.n_shared} shared I={w.I} top-{w.k}, "
+            f"route method {w.method}, {w.act} activations, {w.wdt} weights")
+
+
+def workload_summary(res, cal, fp8_act=False, traffic=True):
+    """tokens/s, ms per step, FC1 / FC2 rooflines and the grouped-GEMM summary of
+    one run_workload result."""
+    w = res["w"]
+    pk, la = res["per_kernel"], res["launches"]
+    tr = (lambda fc: load_traffic(w.name, fc)) if traffic and not fp8_act else (lambda fc: None)
+    out = {"workload": describe(w),
+           "value": round(w.T / (res["ms"] * 1e-3), 1), "unit": "tokens/s",
+           "ms_per_step": round(res["ms"], 4),
+           "roofline": add_calibrated(roofline(w, res["touched"], pk["fc1"], "fc1", tr("fc1"),
+                                               la["fc1"], fp8_act), cal, fp8_act),
+           "roofline_fc2": add_calibrated(roofline(w, res["touched"], pk["fc2"], "fc2", tr("fc2"),
+                                                   la["fc2"], fp8_act), cal, fp8_act),
+           "grouped_gemm": grouped_gemm_summary(w, res["touched"], pk, fp8_act),
+           "per_kernel_ms": pk,
+           "step_stats": res["step_stats"],
+           "rows_per_expert": res["histogram"]}
+    if res["fused"]:
+        out["fused_ffn"] = fused_summary(w, res["touched"], res["fused"], pk, fp8_act)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3_prefill")
-    ap.add_argument("--decode-workload", default="dsv3_decode")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="dsv3_prefill", help="the headline workload")
+    ap.add_argument("--workloads", nargs="*", default=None,
+                    help="workloads to run (default: all five; the headline is always run)")
     ap.add_argument("--fp8act-workloads", nargs="*", default=["dsv3_prefill_fp8", "dsv3_decode_fp8"],
                     help="workloads also run on the fp8-activation path (none: skip)")
-    ap.add_argument("--no-fused", action="store_true",
-                    help="skip timing the fused FC1+FC2 kernel beside each workload")
+    ap.add_argument("--fused", action="store_true",
+                    help="also time the fused FC1+FC2 kernel beside each workload")
     ap.add_argument("--no-routing", action="store_true",
                     help="skip timing moe_route alone for every routing method")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU oracle time budget per workload (token sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
-                    help="skip the measured-peak calibration (copy and library GEMMs)")
+                    help="skip the measured-peak calibration (streams and library GEMMs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -497,94 +591,63 @@ def main():
     cal = None if args.no_calibration else calibrate(dev)
     if cal:
         log(f"[bench] calibration {cal}")
-    fz = not args.no_fused
-    main_res = run_workload(args.workload, args.steps, args.warmup, dev, fused=fz)
-    w = main_res["w"]
-    traffic = load_traffic(args.workload)
-    rl = roofline(w, main_res["touched"], main_res["per_kernel"][DOMINANT], traffic=traffic,
-                  launches=main_res["launches"][DOMINANT])
+    names = WORKLOAD_ORDER if args.workloads is None else list(args.workloads)
+    names = [args.workload] + [n for n in names if n != args.workload]
+    summaries = {}
+    head = None
+    for name in names:
+        res = run_workload(name, args.steps, args.warmup, dev, fused=args.fused)
+        summaries[name] = workload_summary(res, cal)
+        if not args.no_cpu_baseline:
+            summaries[name]["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+            log(f"[bench] {name} cpu baseline {summaries[name]['cpu_baseline']}")
+        if name == args.workload:
+            head = res["w"]
+        del res
+        torch.cuda.empty_cache()
+    hs = summaries[args.workload]
     out = {
         "metric": "MoE layer tokens/s + grouped-GEMM %MFMA / %HBM peak, DSV3 shapes T=512/8192",
-        "value": round(w.T / (main_res["ms"] * 1e-3), 1),
+        "value": hs["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_res["ms"], 4),
+        "ms_per_step": hs["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.act == "bf16" else "f32",
+        "dtype": "bf16" if head.act == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E}+{w.n_shared} shared "
-                               f"I={w.I} top-{w.k}, route method {w.method}, "
-                               f"{w.act} activations, {w.wdt} weights",
-                   "global_batch": w.T, "parallelism": "single GPU, all experts local"},
-        "roofline": add_calibrated(rl, cal),
-        "roofline_fc2": add_calibrated(roofline(w, main_res["touched"], main_res["per_kernel"]["fc2"],
-                                                "fc2", launches=main_res["launches"]["fc2"]), cal),
-        "grouped_gemm": grouped_gemm_summary(w, main_res["touched"], main_res["per_kernel"]),
-        "per_kernel_ms": main_res["per_kernel"],
-        "step_stats": main_res["step_stats"],
-        "rows_per_expert": main_res["histogram"],
+        "config": {"workload": describe(head), "global_batch": head.T,
+                   "parallelism": "single GPU, all experts local"},
+        "roofline": hs["roofline"],
+        "roofline_fc2": hs["roofline_fc2"],
+        "grouped_gemm": hs["grouped_gemm"],
+        "per_kernel_ms": hs["per_kernel_ms"],
+        "step_stats": hs["step_stats"],
+        "rows_per_expert": hs["rows_per_expert"],
         "calibration": cal,
     }
-    if main_res["fused"]:
-        out["fused_ffn"] = fused_summary(w, main_res["touched"], main_res["fused"], main_res["per_kernel"])
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
-        log(f"[bench] cpu baseline {out['cpu_baseline']}")
-    del main_res
-    torch.cuda.empty_cache()
-    if not args.no_decode:
-        d = run_workload(args.decode_workload, args.steps, args.warmup, dev, fused=fz)
-        dw = d["w"]
-        out["decode"] = {
-            "workload": f"{dw.name}: T={dw.T} H={dw.H} E={dw.E} I={dw.I} top-{dw.k}",
-            "value": round(dw.T / (d["ms"] * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(d["ms"], 4),
-            "roofline": add_calibrated(roofline(dw, d["touched"], d["per_kernel"][DOMINANT],
-                                                traffic=load_traffic(args.decode_workload),
-                                                launches=d["launches"][DOMINANT]), cal),
-            "roofline_fc2": add_calibrated(roofline(dw, d["touched"], d["per_kernel"]["fc2"], "fc2",
-                                                    launches=d["launches"]["fc2"]), cal),
-            "grouped_gemm": grouped_gemm_summary(dw, d["touched"], d["per_kernel"]),
-            "per_kernel_ms": d["per_kernel"],
-            "step_stats": d["step_stats"],
-            "rows_per_expert": d["histogram"],
-        }
-        if d["fused"]:
-            out["decode"]["fused_ffn"] = fused_summary(dw, d["touched"], d["fused"], d["per_kernel"])
-        del d
-        torch.cuda.empty_cache()
+    if "cpu_baseline" in hs:
+        out["cpu_baseline"] = hs["cpu_baseline"]
+    if "fused_ffn" in hs:
+        out["fused_ffn"] = hs["fused_ffn"]
+    out["workloads"] = summaries
     if args.fp8act_workloads:
         out["fp8_activations"] = {}
         for name in args.fp8act_workloads:
-            r = run_workload(name, args.steps, args.warmup, dev, fp8_act=True, fused=fz)
-            rw = r["w"]
-            out["fp8_activations"][name] = {
-                "workload": f"{rw.name}: T={rw.T} H={rw.H} E={rw.E}+{rw.n_shared} shared I={rw.I} "
-                            f"top-{rw.k}; x and h quantised to e4m3 in 1x128 blocks, fp8 weights "
-                            f"(128x128 block scales), fp8 MFMA, bf16 output",
-                "value": round(rw.T / (r["ms"] * 1e-3), 1), "unit": "tokens/s",
-                "ms_per_step": round(r["ms"], 4), "dtype": "fp8 e4m3 x e4m3, fp32 accumulate",
-                "roofline": add_calibrated(roofline(rw, r["touched"], r["per_kernel"][DOMINANT],
-                                                    launches=r["launches"][DOMINANT], fp8_act=True),
-                                           cal, fp8_act=True),
-                "roofline_fc2": add_calibrated(roofline(rw, r["touched"], r["per_kernel"]["fc2"], "fc2",
-                                                        launches=r["launches"]["fc2"], fp8_act=True),
-                                               cal, fp8_act=True),
-                "grouped_gemm": grouped_gemm_summary(rw, r["touched"], r["per_kernel"], fp8_act=True),
-                "per_kernel_ms": r["per_kernel"],
-                "step_stats": r["step_stats"],
-            }
-            if r["fused"]:
-                out["fp8_activations"][name]["fused_ffn"] = fused_summary(
-                    rw, r["touched"], r["fused"], r["per_kernel"], fp8_act=True)
+            r = run_workload(name, args.steps, args.warmup, dev, fp8_act=True, fused=args.fused)
+            o = workload_summary(r, cal, fp8_act=True)
+            o["workload"] = (f"{r['w'].name}: T={r['w'].T} H={r['w'].H} E={r['w'].E}+{r['w'].n_shared} "
+                             f"shared I={r['w'].I} top-{r['w'].k}; x and h quantised to e4m3 in 1x128 "
+                             f"blocks, fp8 weights (128x128 block scales), fp8 MFMA, bf16 output")
+            o["dtype"] = "fp8 e4m3 x e4m3, fp32 accumulate"
+            out["fp8_activations"][name] = o
             del r
             torch.cuda.empty_cache()
     if not args.no_routing:
-        out["routing"] = routing_summary([args.workload, args.decode_workload], dev)
+        out["routing"] = routing_summary(["dsv3_prefill", "dsv3_decode"], dev)
     print(json.dumps(out), flush=True)
 
 

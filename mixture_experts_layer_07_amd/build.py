@@ -1,4 +1,5 @@
-"""Build libmoe.so (the gfx950 HIP library behind include/moe.h) in-tree.
+"""Build libmoe.so (the gfx950 HIP library behind include/moe.h) and the
+benchmark's calibration library libmoe_calib.so in-tree.
 
     python -m mixture_experts_layer_07_amd.build
 """
@@ -12,6 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "fused.hip", "finalize.hip",
            "quant.hip", "noalloc.hip"]
+CALIB_SOURCE = "calib.hip"
+CALIB_LIB = os.path.join(HERE, "libmoe_calib.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -52,6 +55,16 @@ def build(verbose: bool = True, jobs: int = 5) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB, flush=True)
+    # the benchmark's HBM read calibration kernel, a library of its own
+    obj = compile_one(CALIB_SOURCE)
+    tmp = CALIB_LIB + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stdout + r.stderr))
+    os.replace(tmp, CALIB_LIB)
+    if verbose:
+        print("built", CALIB_LIB, flush=True)
     return LIB
 
 
