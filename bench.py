@@ -336,6 +336,63 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
         print(json.dumps(out, indent=1))
 
 
+LIB_KERNELS = {"route_kernel", "permute_count_kernel", "permute_scan_kernel", "permute_scatter_kernel",
+               "finalize_kernel", "quantize_fp8_kernel", "grouped_gemm_kernel", "fused_ffn_kernel"}
+
+
+def class_summary(pmc_dirs, trace_dir):
+    """Markdown table per kernel (grouped-GEMM row classes separately) from
+    rocprofv3 --pmc runs (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_BUSY_CU_CYCLES, SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY, TCC_HIT_sum,
+    TCC_MISS_sum; per dispatch) and a --kernel-trace run of the same command
+    (median duration): MFMA-busy fraction of the CU-busy cycles, the fraction
+    of wave cycles spent waiting on a counter, the L2 hit rate and the mean
+    clock (GPU-busy cycles per XCD over the kernel's duration)."""
+    import csv
+    import glob
+    import re
+    from collections import defaultdict
+
+    def cls(n):
+        m = re.search(r"dma_gemm_kernel<(\d), moe::\(anonymous namespace\)::DmaCfg<(\d+), (\d+), (\d+), "
+                      r"(\d+), (\d+), (\d+)", n)
+        if m:
+            kind = " fp8 x fp8" if "true, true" in n else (" fp8 weights" if "true, false" in n else "")
+            return (f"FC{int(m.group(1)) + 1} {m.group(2)}x{m.group(3)} tiles, "
+                    f"{int(m.group(4)) * int(m.group(5))} waves, group-M {m.group(6)}, "
+                    f"ring {m.group(7)}{kind}")
+        m = re.search(r"(\w+_kernel)(<[^(]*>)?", n)
+        return m.group(0) if m else n[:40]
+    agg, disp, dur = defaultdict(lambda: defaultdict(float)), defaultdict(set), defaultdict(list)
+    for d in pmc_dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                c = cls(r["Kernel_Name"])
+                agg[c][r["Counter_Name"]] += float(r["Counter_Value"])
+                disp[(c, r["Counter_Name"])].add(r["Dispatch_Id"])
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            dur[cls(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    n_xcd = 8
+    lines = ["| kernel | median us | dispatches | MFMA busy / CU busy | waves waiting | L2 hit | clock GHz |",
+             "|---|---|---|---|---|---|---|"]
+    for c in sorted(dur, key=lambda c: -sorted(dur[c])[len(dur[c]) // 2]):
+        ds = sorted(dur[c])
+        med = ds[len(ds) // 2]
+        if med < 10 or not (c.startswith("FC") or c.split("<")[0] in LIB_KERNELS):
+            continue
+        a = agg.get(c, {})
+        per = lambda k: a.get(k, 0.0) / max(1, len(disp.get((c, k), ())))  # noqa: E731
+        busy = a.get("SQ_BUSY_CU_CYCLES", 0.0)
+        mf = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * busy) if busy else float("nan")
+        wt = a.get("SQ_WAIT_INST_ANY", 0.0) / a["SQ_WAVE_CYCLES"] if a.get("SQ_WAVE_CYCLES") else float("nan")
+        h, m = a.get("TCC_HIT_sum", 0.0), a.get("TCC_MISS_sum", 0.0)
+        l2 = h / (h + m) if h + m else float("nan")
+        clk = per("GRBM_GUI_ACTIVE") / n_xcd / (med * 1e3) if per("GRBM_GUI_ACTIVE") else float("nan")
+        lines.append(f"| {c} | {med:.1f} | {len(ds)} | {mf:.3f} | {wt:.3f} | {l2:.3f} | {clk:.2f} |")
+    print("\n".join(lines))
+
+
 def time_layer(layer, inp, steps, warmup):
     """ms per step of layer(inp) and its per-kernel ms per step (HIP-event hooks
     on, in a second pass of as many steps)."""
@@ -572,7 +629,13 @@ def main():
                     help="summarize two rocprofv3 --pmc runs into profiles/ and exit")
     ap.add_argument("--traffic-command", action="append", default=[],
                     help="command lines recorded in the traffic summary")
+    ap.add_argument("--class-summary", nargs="+", metavar="DIR",
+                    help="print per-kernel counter table: rocprofv3 --pmc output dirs, then the "
+                         "--kernel-trace dir of the same command (last argument), and exit")
     args = ap.parse_args()
+    if args.class_summary:
+        class_summary(args.class_summary[:-1], args.class_summary[-1])
+        return
     if args.traffic_from:
         summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.workload,
                           args.calibrate_copy_mib, args.traffic_command)
