@@ -7,7 +7,8 @@
 // Three small kernels over fixed chunks of kChunk consecutive pairs:
 //   count    per-chunk histogram of expert ids (LDS counters)
 //   scan     per expert, exclusive scan of its chunk counts -> the base row of
-//            each (chunk, expert); exclusive scan over experts -> offsets
+//            each (chunk, expert); exclusive scan over experts (wavefront
+//            shuffle scans, then the four wavefront totals) -> offsets
 //   scatter  one wavefront per chunk walks its pairs in order, 64 at a time;
 //            lanes holding the same expert find each other with one ballot per
 //            id bit, take rank = #peers on lower lanes, and the highest peer
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
                                                            int32_t* __restrict__ offsets)
 {
     constexpr int kBatch = 16;  // loads in flight per thread (the column walk is latency bound)
-    __shared__ int tot[256];
+    __shared__ int wtot[4];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
@@ -58,16 +59,20 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
             for (int j = 0; j < kBatch; ++j) run += v[j];
         }
     }
-    tot[e] = (e < E) ? run : 0;
-    __syncthreads();
-    // inclusive scan over experts (Hillis-Steele)
-    for (int d = 1; d < 256; d <<= 1) {
-        const int v = (e >= d) ? tot[e - d] : 0;
-        __syncthreads();
-        tot[e] += v;
-        __syncthreads();
+    // exclusive scan over experts: an inclusive scan within each wavefront
+    // (six shuffle steps), then the four wavefront totals through LDS
+    const int lane = e & 63, wave = e >> 6;
+    int incl = (e < E) ? run : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
     }
-    const int base = (e < E) ? tot[e] - run : 0;
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    const int base = (e < E) ? before + incl - run : 0;
     if (e < E) {
         offsets[e] = base;
         // pass 2: each chunk's count becomes its first row for this expert
