@@ -958,10 +958,12 @@ moe_status run_gemm(FfnArgs args, int lo_rows, int hi_rows, int R, hipStream_t s
     return launch_status(MODE == FC1 ? "fc1 grouped_gemm_kernel" : "fc2 grouped_gemm_kernel");
 }
 
-// Row classes: each group goes to the tile shape that suits its row count.
+// Row classes: each group goes to the tile shape that suits its row count
+// (bf16 shapes; the fp8-weight and fp8 x fp8 shapes are listed at their
+// dispatch functions below).
 //   [0, 64)     32x128 tiles, 4 waves: weight streaming for decode-like groups
-//   [64, 384)   128x256 tiles, 8 waves
-//   [384, inf)  256x256 tiles, 8 waves: MFMA-bound groups
+//   [64, 384)   128x256 tiles, 16 waves
+//   [384, inf)  256x256 tiles, 16 waves: MFMA-bound groups
 constexpr int kMidRows = 64;
 constexpr int kBigRows = 384;
 constexpr int kAllRows = 1 << 30;
