@@ -336,7 +336,8 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, commands):
         print(json.dumps(out, indent=1))
 
 
-LIB_KERNELS = {"route_kernel", "permute_count_kernel", "permute_scan_kernel", "permute_scatter_kernel",
+LIB_KERNELS = {"route_kernel", "permute_one_kernel", "permute_count_kernel", "permute_scan_kernel",
+               "permute_scatter_kernel",
                "finalize_kernel", "quantize_fp8_kernel", "grouped_gemm_kernel", "fused_ffn_kernel"}
 
 

@@ -350,7 +350,8 @@ enum {
     MOE_KID_FINALIZE = 6,
     MOE_KID_QUANT = 7,
     MOE_KID_FFN_FUSED = 8,
-    MOE_NUM_KIDS = 9
+    MOE_KID_PERMUTE_ONE = 9,   /* the one-workgroup permute (inputs of up to 8192 pairs) */
+    MOE_NUM_KIDS = 10
 };
 moe_status moe_timing_enable(int enable);
 moe_status moe_kernel_times(double* ms /*[MOE_NUM_KIDS]*/, int64_t* launches /*[MOE_NUM_KIDS]*/,

@@ -21,7 +21,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 ROUTE_DEFAULT, ROUTE_RENORMALIZE, ROUTE_DEEPSEEKV3, ROUTE_RENORMALIZE_NAIVE = 0, 1, 2, 4
 ROUTE_FLAG_RENORMALIZE = 1
 KERNEL_IDS = ["route", "permute_count", "permute_scan", "permute_scatter", "fc1", "fc2",
-              "finalize", "quantize", "ffn_fused"]
+              "finalize", "quantize", "ffn_fused", "permute_one"]
 FUSED_MAX_I = 2048
 NOALLOC_SCRATCH_BYTES = 64 << 20
 

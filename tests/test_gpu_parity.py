@@ -116,10 +116,13 @@ def test_route_special_values():
 
 
 # ------------------------------------------------------------------ permute
+# Up to 8192 pairs the permute is one workgroup; above, three chunked
+# kernels: both sides of the switch, and its edge, are covered.
 @pytest.mark.parametrize("T,k,E,n_shared,dist", [
     (1, 1, 1, 0, "uniform"), (333, 2, 8, 0, "uniform"), (4096, 8, 256, 1, "uniform"),
     (8192, 8, 256, 1, "zipf"), (2048, 8, 128, 0, "one"), (1500, 3, 7, 2, "uniform"),
-    (130, 8, 256, 0, "uniform"),
+    (130, 8, 256, 0, "uniform"), (512, 8, 256, 0, "zipf"), (1024, 8, 64, 0, "one"),
+    (8192, 1, 64, 0, "uniform"), (8193, 1, 64, 0, "uniform"), (9000, 8, 256, 1, "zipf"),
 ])
 def test_permute_parity(T, k, E, n_shared, dist):
     rng = np.random.default_rng(T + k + E)
@@ -401,8 +404,11 @@ def test_kernel_timing_hooks():
         t = moe.kernel_times(reset=True)
     finally:
         moe.timing_enable(False)
-    for name in ("route", "permute_count", "permute_scan", "permute_scatter", "finalize"):
+    # 512 pairs: the one-workgroup permute, not the chunked kernels
+    for name in ("route", "permute_one", "finalize"):
         assert t[name][1] == 3 and t[name][0] > 0, (name, t[name])
+    for name in ("permute_count", "permute_scan", "permute_scatter"):
+        assert t[name][1] == 0, (name, t[name])
     # each grouped GEMM is one launch per row class (same count every call)
     for name in ("fc1", "fc2"):
         assert t[name][1] >= 3 and t[name][1] % 3 == 0 and t[name][0] > 0, (name, t[name])
