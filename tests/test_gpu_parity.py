@@ -136,6 +136,22 @@ def test_permute_parity(T, k, E, n_shared, dist):
     check_permute(ids.astype(np.int32), E, n_shared)
 
 
+@pytest.mark.parametrize("T,k,E", [(300, 4, 64), (2000, 8, 256)])
+def test_permute_clamps_out_of_range_ids(T, k, E):
+    """Ids outside [0, E) are clamped into range (the boundary's reading of
+    such input): the result is the stable sort of the clipped ids.  One case
+    on each side of the one-workgroup switch (1200 and 16000 pairs)."""
+    rng = np.random.default_rng(T * k)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.05
+    ids[bad] = rng.choice(np.array([-1, -1000, E, E + 7, 2**31 - 1], np.int64), size=int(bad.sum())).astype(np.int32)
+    off_g, pp_g, up_g = moe.permute(torch.from_numpy(ids).to(DEV), E, 0)
+    off_o, pp_o, up_o = oracle.permute(np.clip(ids, 0, E - 1).astype(np.int32), E, 0)
+    assert np.array_equal(host(off_g).numpy(), off_o)
+    assert np.array_equal(host(pp_g).numpy(), pp_o)
+    assert np.array_equal(host(up_g).numpy(), up_o)
+
+
 # ------------------------------------------------------------ expert FFN
 def small_workload(act, wdt, T=300, H=384, I=256, E=8, k=2, n_shared=0, method=4, **kw):
     return wl.Workload(f"small_{act}_{wdt}", 96, T=T, H=H, E=E, I=I, k=k, method=method,
